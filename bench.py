@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Throughput of the triangle multiplicative update on one MI355X.
+
+One step = one forward call (stage 1 LayerNorm_in + gated projections, stage 2
+contraction, stage 3 LayerNorm_out + gated output projection) over the
+N = 768, c_z = c = 128, B = 1 workload with inputs already resident in HBM.
+The timed loop enqueues the three stages through the C ABI with HIP events
+between them, so the per-stage device times come from the same timed region.
+
+Prints ONE JSON line (rank 0). Extra legs: the roofline of the dominant stage
+and the CPU oracle's time on this host (a baseline, not a target).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_FILES = {1: "k1_ln_proj.hip", 2: "k2_contract.hip", 3: "k3_epilogue.hip"}
+KERNEL_NAMES = {1: "k1_ln_proj", 2: "k2_contract", 3: "k3_epilogue"}
+MFMA_BALANCE = 2516.6e12 / 8000e9       # flop per byte where the two roofs meet
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: the N=768 one)")
+    ap.add_argument("--direction", default="outgoing", choices=["outgoing", "incoming"])
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--cpu-sample-rows", type=int, default=0,
+                    help="time the oracle on this many output rows only (0 = the whole call)")
+    return ap.parse_args()
+
+
+def kernel_sha(stage: int) -> str:
+    csrc = os.path.join(ROOT, "triangle_multiplicative_update_amd", "csrc")
+    h = hashlib.sha256()
+    for f in (KERNEL_FILES[stage], "trimul_device.hpp", "trimul_kernels.hpp"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(stage: int, workload: str, direction: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{KERNEL_NAMES[stage]}_{workload}_{direction}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_sha") != kernel_sha(stage):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, wl, direction, flops_per_call, sample_rows: int):
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+                      or [1])
+    except Exception:
+        threads = 1
+    import oracle
+    t0 = time.perf_counter()
+    if sample_rows and sample_rows < wl.N:
+        rows = list(range(sample_rows))
+        oracle.forward_block(inp, direction, rows, list(range(wl.N)))
+        dt = time.perf_counter() - t0
+        frac = sample_rows / wl.N
+        sample = f"oracle.forward_block over {sample_rows} of {wl.N} output rows (all columns)"
+    else:
+        oracle.forward(inp, direction)
+        dt = time.perf_counter() - t0
+        frac = 1.0
+        sample = f"oracle.forward, the whole {wl.name} {direction} call"
+    del np
+    return {
+        "value": flops_per_call * frac / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": sample,
+        "seconds": dt,
+        "pair_cells_per_s": wl.B * wl.N * wl.N * frac / dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synthetic_inputs as si
+    from triangle_multiplicative_update_amd import perf_model
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}), flush=True)
+        sys.exit(1)
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    name = args.workload or si.BENCH_WORKLOAD
+    wl = si.WORKLOADS[name]
+    direction = args.direction
+    inp = si.generate(wl)
+
+    def up(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    d = {k: up(v) for k, v in inp.items()}
+    from triangle_multiplicative_update_amd.api import workspace_bytes
+    out = torch.empty_like(d["x"])
+    ws = torch.empty(workspace_bytes(wl.B, wl.N, wl.c, direction), dtype=torch.uint8, device=dev)
+    from triangle_multiplicative_update_amd.api import Prepared
+    prep = Prepared(d["x"], direction, d["mask"], {k: d[k] for k in si.PARAM_NAMES}, out, ws)
+
+    with torch.no_grad():
+        for _ in range(args.warmup):
+            prep.forward()
+        torch.cuda.synchronize()
+
+        K = args.steps
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(K):
+            ev[k][0].record()
+            prep.stage(1)
+            ev[k][1].record()
+            prep.stage(2)
+            ev[k][2].record()
+            prep.stage(3)
+            ev[k][3].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+
+    per_stage_ms = [float(np.mean([ev[k][s].elapsed_time(ev[k][s + 1]) for k in range(K)]))
+                    for s in range(3)]
+    span_ms = ev[0][0].elapsed_time(ev[K - 1][3]) / K      # device span per step
+    ms_per_step = wall * 1e3 / K                            # host clock, synchronized both sides
+    F = perf_model.flops(wl.B, wl.N, wl.c_z, wl.c)
+    T = perf_model.traffic_bytes(wl.B, wl.N, wl.c_z, wl.c, mask=inp["mask"] is not None)
+    t = ms_per_step * 1e-3
+    tflops = F / t / 1e12
+
+    sf = perf_model.stage_flops(wl.B, wl.N, wl.c_z, wl.c)
+    sb = perf_model.stage_bytes(wl.B, wl.N, wl.c_z, wl.c, mask=inp["mask"] is not None)
+    dom = int(np.argmax(per_stage_ms))
+    ts = per_stage_ms[dom] * 1e-3
+    intensity = sf[dom] / sb[dom]
+    if intensity > MFMA_BALANCE:
+        roof = {"bound": "mfma", "achieved": sf[dom] / ts / 1e12, "peak": perf_model.PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": sb[dom] / ts / 1e9, "peak": perf_model.PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(dom + 1, name, direction)
+    roof["kernel"] = KERNEL_NAMES[dom + 1]
+    roof["kernel_us"] = per_stage_ms[dom] * 1e3
+    roof["algorithmic_bytes"] = sb[dom]
+    roof["algorithmic_flops"] = sf[dom]
+
+    line = {
+        "metric": "TFLOP/s and pair-cells/s (B*N^2/s) at N=768, c=128, bf16; % of MFMA peak",
+        "value": tflops,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "B": wl.B, "N": wl.N, "c_z": wl.c_z, "c": wl.c,
+                   "direction": direction, "mask": wl.mask if wl.mask != "padded" else f"padded L={wl.mask_len}",
+                   "biases": wl.biases},
+        "pair_cells_per_s": wl.B * wl.N * wl.N / t,
+        "pct_mfma_peak": 100.0 * tflops / perf_model.PEAK_BF16_TFLOPS,
+        "hbm_gbs_model": T / t / 1e9,
+        "per_stage_us": {KERNEL_NAMES[s + 1]: per_stage_ms[s] * 1e3 for s in range(3)},
+        "device_ms_per_step": span_ms,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, wl, direction, F, args.cpu_sample_rows)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

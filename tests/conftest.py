@@ -27,3 +27,14 @@ def gpu():
         pytest.skip("no GPU visible")
     import torch
     return torch.device("cuda", 0)
+
+
+def _ensure_library():
+    """Build libtrimul.so only when nothing is built (normally build() ran first)."""
+    lib = os.path.join(ROOT, "triangle_multiplicative_update_amd", "libtrimul.so")
+    if not os.path.exists(lib):
+        from triangle_multiplicative_update_amd.build import build
+        build()
+
+
+_ensure_library()

@@ -1,0 +1,199 @@
+"""GPU checks of the intermediate planes, canaries, determinism and identities.
+
+The workspace layout (a, b, y planes, channel-major, documented in
+include/trimul.h) is part of the contract, so the tests read the planes after a
+call and compare them with the oracle's bf16 intermediates.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from parity_utils import (assert_within_tolerance, bf16_to_f64, bf16_ulp_distance, call, planes,
+                          plane_layout, say, to_device)
+from triangle_multiplicative_update_amd import workspace_bytes
+
+pytestmark = pytest.mark.gpu
+
+
+def _ws(B, N, c, direction, device, fill=None):
+    n = workspace_bytes(B, N, c, direction)
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    if fill is not None:
+        ws.view(torch.bfloat16).fill_(fill)
+    return ws
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+@pytest.mark.parametrize("B,N,c", [(1, 136, 128), (2, 77, 128), (1, 72, 256)])
+def test_planes_match_oracle(gpu, direction, B, N, c):
+    wl = si.custom(B, N, c, mask="bernoulli", mask_p=0.8, seed=7 + N)
+    inp = si.generate(wl)
+    say(f"[gpu] planes {wl.name} {direction}")
+    d = to_device(inp, gpu)
+    ws = _ws(B, N, c, direction, gpu, fill=float("nan"))
+    with torch.no_grad():
+        out = call(d, direction, workspace=ws)
+    torch.cuda.synchronize()
+    ref = oracle.forward(inp, direction)
+    pa, pb, py = planes(ws, B, N, c)
+    for name, plane, want in (("a", pa, ref.a), ("b", pb, ref.b), ("y", py, ref.y)):
+        got = bf16_to_f64(plane[:, :, :N])
+        exp = plane_layout(want, direction, name)
+        ulps = bf16_ulp_distance(got, exp)
+        frac = np.count_nonzero(ulps) / ulps.size
+        say(f"[planes] {name}: mismatch fraction {frac:.2e}, max ulps {ulps.max()}")
+        # fp32 vs fp64 before the single rounding: rare one-ulp flips only
+        # (y also inherits the flips of a and b through the sum).
+        assert ulps.max() <= (1 if name != "y" else 2), name
+        assert frac <= (1e-2 if name != "y" else 0.2), name
+        if name != "y":
+            # padded plane columns are written as +0.0
+            n_pad = plane.shape[-1]
+            if n_pad > N:
+                tail = plane[:, :, N:].float().cpu().numpy()
+                assert np.all(tail == 0) and not np.any(np.signbit(tail)), name
+    # the output itself
+    assert_within_tolerance(bf16_to_f64(out), ref.out, f"{wl.name} {direction}")
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_masked_rows_are_positive_zero(gpu, direction):
+    B, N, c, L = 1, 100, 128, 70
+    wl = si.custom(B, N, c, mask="padded", mask_len=L, seed=3)
+    inp = si.generate(wl)
+    say(f"[gpu] masked zeros {wl.name} {direction}")
+    d = to_device(inp, gpu)
+    ws = _ws(B, N, c, direction, gpu, fill=float("nan"))
+    with torch.no_grad():
+        call(d, direction, workspace=ws)
+    torch.cuda.synchronize()
+    pa, pb, py = planes(ws, B, N, c)
+    for name, plane in (("a", pa), ("b", pb), ("y", py)):
+        v = plane[:, :, :N].float().cpu().numpy()        # [c, N, N] (row, column)
+        pad = np.zeros((N, N), bool)
+        pad[L:, :] = True
+        pad[:, L:] = True
+        z = v[:, pad]
+        assert np.all(z == 0) and not np.any(np.signbit(z)), name
+        assert np.count_nonzero(v[:, ~pad]) > 0.9 * v[:, ~pad].size, name
+
+
+def test_nan_canary_and_determinism(gpu):
+    wl = si.custom(2, 130, 128, mask="bernoulli", seed=11)
+    inp = si.generate(wl)
+    say(f"[gpu] canary {wl.name}")
+    d = to_device(inp, gpu)
+    B, N, c = 2, 130, 128
+    outs = []
+    for rep in range(3):
+        ws = _ws(B, N, c, "outgoing", gpu, fill=float("nan"))
+        out = torch.full((B, N, N, c), float("nan"), dtype=torch.bfloat16, device=gpu)
+        with torch.no_grad():
+            call(d, "outgoing", out=out, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out).all()
+        outs.append(out.view(torch.int16).cpu())
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+def test_direction_identity_on_gpu(gpu):
+    """y of the incoming direction on x equals y of the outgoing direction on x
+    with its pair axes swapped (and the mask likewise)."""
+    B, N, c = 1, 96, 128
+    wl = si.custom(B, N, c, mask="bernoulli", seed=21)
+    inp = si.generate(wl)
+    inp_t = dict(inp)
+    inp_t["x"] = np.ascontiguousarray(np.swapaxes(inp["x"], 1, 2))
+    inp_t["mask"] = np.ascontiguousarray(np.swapaxes(inp["mask"], 1, 2))
+    say("[gpu] direction identity")
+    ws1 = _ws(B, N, c, "incoming", gpu)
+    ws2 = _ws(B, N, c, "outgoing", gpu)
+    with torch.no_grad():
+        call(to_device(inp, gpu), "incoming", workspace=ws1)
+        call(to_device(inp_t, gpu), "outgoing", workspace=ws2)
+    torch.cuda.synchronize()
+    y1 = planes(ws1, B, N, c)[2][:, :, :N].view(torch.int16).cpu()
+    y2 = planes(ws2, B, N, c)[2][:, :, :N].view(torch.int16).cpu()
+    assert torch.equal(y1, y2)
+
+
+def test_mask_none_equals_ones_and_biases_none_equal_zero(gpu):
+    B, N, c = 1, 70, 128
+    wl = si.custom(B, N, c, mask="ones", seed=5)
+    inp = si.generate(wl)
+    say("[gpu] mask None / zero biases equivalence")
+    d = to_device(inp, gpu)
+    with torch.no_grad():
+        o1 = call(d, "outgoing")
+        o2 = call(d, "outgoing", mask=None)
+        dz = dict(d)
+        for k in ("p_in_bias", "g_in_bias", "p_out_bias", "g_out_bias"):
+            dz[k] = torch.zeros_like(d[k])
+        dn = dict(d)
+        for k in ("p_in_bias", "g_in_bias", "p_out_bias", "g_out_bias"):
+            dn[k] = None
+        o3 = call(dz, "outgoing")
+        o4 = call(dn, "outgoing")
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+    # equal up to the sign of zero
+    assert torch.equal(o3.float(), o4.float())
+
+
+def test_stages_chain_equals_forward(gpu):
+    B, N, c = 1, 88, 128
+    wl = si.custom(B, N, c, mask="bernoulli", seed=8)
+    inp = si.generate(wl)
+    say("[gpu] stage chain == forward")
+    d = to_device(inp, gpu)
+    with torch.no_grad():
+        o1 = call(d, "incoming")
+        ws = _ws(B, N, c, "incoming", gpu)
+        o2 = torch.empty_like(o1)
+        for s in (1, 2, 3):
+            call(d, "incoming", out=o2, workspace=ws, stage=s)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_batchless_and_mask_dtypes(gpu):
+    N, c = 40, 128
+    wl = si.custom(1, N, c, mask="bernoulli", seed=9)
+    inp = si.generate(wl)
+    say("[gpu] batchless and mask dtypes")
+    d = to_device(inp, gpu)
+    with torch.no_grad():
+        o_ref = call(d, "outgoing")
+        db = dict(d)
+        db["x"] = d["x"][0]
+        o_bl = call(db, "outgoing", mask=d["mask"][0].bool())
+        o_f32 = call(d, "outgoing", mask=d["mask"].float())
+    torch.cuda.synchronize()
+    assert o_bl.shape == (N, N, c)
+    assert torch.equal(o_bl.view(torch.int16), o_ref[0].view(torch.int16))
+    assert torch.equal(o_f32.view(torch.int16), o_ref.view(torch.int16))
+
+
+def test_declines_on_device(gpu):
+    from triangle_multiplicative_update_amd import triangle_multiplicative_update
+    N, c = 16, 128
+    wl = si.custom(1, N, c, mask="ones", seed=1)
+    d = to_device(si.generate(wl), gpu)
+    with torch.no_grad():
+        with pytest.raises(ValueError):
+            call(d, "sideways")
+        with pytest.raises(ValueError):   # out aliases x
+            call(d, "outgoing", out=d["x"])
+        with pytest.raises(NotImplementedError):
+            triangle_multiplicative_update(d["x"], "outgoing", None, *[d[k] for k in (
+                "norm_in_weight", "norm_in_bias", "p_in_weight", "p_in_bias", "g_in_weight",
+                "g_in_bias", "norm_out_weight", "norm_out_bias", "p_out_weight", "p_out_bias",
+                "g_out_weight", "g_out_bias")], precision="tf32")
+    xg = d["x"].clone().requires_grad_(True)
+    dg = dict(d)
+    dg["x"] = xg
+    with pytest.raises(NotImplementedError):
+        call(dg, "outgoing")

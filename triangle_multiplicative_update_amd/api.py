@@ -1,0 +1,228 @@
+"""Drop-in Python entry point over the gfx950 C ABI.
+
+The signature and behaviour follow the page "Triangle Multiplicative Update
+(SM100 / SM103 / SM107)", section "Drop-in function" (parameter names, order
+and defaults; the keyword-only ``out=`` and ``stream=``), and the declines of
+section "Served today, and the typed declines". PyTorch supplies device memory
+and the stream; every step of the computation runs in the HIP kernels.
+"""
+
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import _native
+from ._native import lib
+
+_DIRECTIONS = {"outgoing": _native.TRIMUL_OUTGOING, "incoming": _native.TRIMUL_INCOMING}
+_SERVED_PRECISION = (None, "default", "none", "bfloat16", "bf16")
+_DECLINED_PRECISION = ("mxfp8", "ieee", "tf32")
+_PARAM_ORDER = ("norm_in_weight", "norm_in_bias", "p_in_weight", "p_in_bias", "g_in_weight",
+                "g_in_bias", "norm_out_weight", "norm_out_bias", "p_out_weight", "p_out_bias",
+                "g_out_weight", "g_out_bias")
+_REQUIRED = ("norm_in_weight", "norm_in_bias", "p_in_weight", "g_in_weight", "norm_out_weight",
+             "norm_out_bias", "p_out_weight", "g_out_weight")
+
+
+def raise_for_status(status: int, what: str = "trimul") -> None:
+    """Map a C-ABI status to the page's typed errors."""
+    if status == _native.TRIMUL_OK:
+        return
+    msg = f"{what}: {_native.last_error()}"
+    if status == _native.TRIMUL_E_INVALID:
+        raise ValueError(msg)
+    if status == _native.TRIMUL_E_UNSUPPORTED:
+        raise NotImplementedError(msg)
+    raise RuntimeError(msg)
+
+
+def workspace_bytes(B: int, N: int, c: int, direction: str = "outgoing") -> int:
+    """Bytes of the a, b, y planes for one call (layout in include/trimul.h)."""
+    return int(lib.trimul_workspace_bytes(B, N, c, _direction_code(direction)))
+
+
+def check_support(B: int, N: int, c_z: int, c: int, direction: str = "outgoing",
+                  device: Optional[int] = None) -> None:
+    """Typed declines with no launch; ``device`` None skips the device check."""
+    st = lib.trimul_check_support(B, N, c_z, c, _direction_code(direction),
+                                  -1 if device is None else int(device))
+    raise_for_status(st, "check_support")
+
+
+def _direction_code(direction) -> int:
+    if direction not in _DIRECTIONS:
+        raise ValueError(f"direction must be 'outgoing' or 'incoming', got {direction!r}")
+    return _DIRECTIONS[direction]
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _prep_param(name, t, precision, device):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, x is on {device}")
+    if t.dtype != torch.bfloat16:
+        if precision in ("bfloat16", "bf16"):
+            t = t.to(torch.bfloat16)
+        else:
+            raise NotImplementedError(
+                f"{name} is {t.dtype}; parameters must be bf16 (or pass precision='bfloat16')")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def triangle_multiplicative_update(
+        x, direction="outgoing", mask=None,
+        norm_in_weight=None, norm_in_bias=None, p_in_weight=None, p_in_bias=None,
+        g_in_weight=None, g_in_bias=None, norm_out_weight=None, norm_out_bias=None,
+        p_out_weight=None, p_out_bias=None, g_out_weight=None, g_out_bias=None,
+        eps=1e-5, precision=None, *, out=None, stream=None, workspace=None,
+        _stage=None) -> torch.Tensor:
+    """Triangle multiplicative update, forward, bf16, on an MI355X (gfx950).
+
+    x: [B, N, N, c_z] or [N, N, c_z] bf16 CUDA/HIP tensor, contiguous.
+    mask: None, or [B, N, N] ([N, N] at B = 1) of any real or bool dtype.
+    Returns out with x's rank (or ``out`` itself when given). The residual add is
+    the caller's. ``workspace``: optional uint8 tensor of at least
+    ``workspace_bytes(B, N, c, direction)`` bytes (allocated per call otherwise).
+    """
+    code = _direction_code(direction)
+    if precision in _DECLINED_PRECISION or precision not in _SERVED_PRECISION:
+        raise NotImplementedError(f"precision={precision!r} is not served "
+                                  f"(served: None, 'default', 'none', 'bfloat16')")
+    if not isinstance(x, torch.Tensor):
+        raise ValueError("x must be a tensor")
+    params = dict(zip(_PARAM_ORDER, (norm_in_weight, norm_in_bias, p_in_weight, p_in_bias,
+                                      g_in_weight, g_in_bias, norm_out_weight, norm_out_bias,
+                                      p_out_weight, p_out_bias, g_out_weight, g_out_bias)))
+    if torch.is_grad_enabled():
+        grads = [n for n, t in [("x", x), ("mask", mask), *params.items()]
+                 if isinstance(t, torch.Tensor) and t.requires_grad]
+        if grads:
+            raise NotImplementedError(
+                f"autograd is not supported (forward only): {grads[0]} requires grad; "
+                "call under torch.no_grad() or detach")
+    for n in _REQUIRED:
+        if params[n] is None:
+            raise ValueError(f"{n} is required")
+    if x.device.type != "cuda":
+        raise ValueError(f"x must be on a GPU device, got {x.device}")
+    if x.dtype != torch.bfloat16:
+        if precision in ("bfloat16", "bf16"):
+            x = x.to(torch.bfloat16)
+        else:
+            raise NotImplementedError(f"x is {x.dtype}; the pair representation must be bf16 "
+                                      "(or pass precision='bfloat16')")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous (no hidden copy is made)")
+    batchless = x.dim() == 3
+    if x.dim() not in (3, 4):
+        raise ValueError(f"x must be [B, N, N, c_z] or [N, N, c_z], got shape {tuple(x.shape)}")
+    xb = x.unsqueeze(0) if batchless else x
+    B, N, N2, c_z = xb.shape
+    if N != N2:
+        raise ValueError(f"x must be square in its pair axes, got {tuple(x.shape)}")
+    device = x.device
+    for n in _PARAM_ORDER:
+        params[n] = _prep_param(n, params[n], precision, device)
+    c = params["p_in_weight"].shape[0] // 2
+    shapes = {"norm_in_weight": (c_z,), "norm_in_bias": (c_z,), "p_in_weight": (2 * c, c_z),
+              "p_in_bias": (2 * c,), "g_in_weight": (2 * c, c_z), "g_in_bias": (2 * c,),
+              "norm_out_weight": (c,), "norm_out_bias": (c,), "p_out_weight": (c_z, c),
+              "p_out_bias": (c_z,), "g_out_weight": (c_z, c_z), "g_out_bias": (c_z,)}
+    for n, shp in shapes.items():
+        t = params[n]
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{n} must have shape {shp}, got {tuple(t.shape)}")
+
+    if mask is not None:
+        if not isinstance(mask, torch.Tensor):
+            raise ValueError("mask must be a tensor or None")
+        if mask.device != device:
+            raise ValueError(f"mask is on {mask.device}, x is on {device}")
+        if mask.dim() == 2 and B == 1:
+            mask = mask.unsqueeze(0)
+        if tuple(mask.shape) != (B, N, N):
+            raise ValueError(f"mask must be [B, N, N] = {(B, N, N)}"
+                             f"{' or [N, N]' if B == 1 else ''}, got {tuple(mask.shape)}")
+        if mask.dtype != torch.bfloat16 or not mask.is_contiguous():
+            mask = mask.to(torch.bfloat16).contiguous()   # cast once per call
+
+    if out is None:
+        out_t = torch.empty_like(xb)
+        ret = out_t[0] if batchless else out_t
+    else:
+        if not isinstance(out, torch.Tensor) or out.dtype != torch.bfloat16:
+            raise ValueError("out must be a bf16 tensor")
+        if out.numel() != xb.numel() or out.shape[-3:] != xb.shape[-3:] or out.device != device:
+            raise ValueError(f"out must be {tuple(xb.shape)} (or batchless at B = 1) on {device}")
+        if not out.is_contiguous():
+            raise ValueError("out must be contiguous")
+        out_t, ret = out, out
+
+    need = workspace_bytes(B, N, c, direction) if c in (128, 256) and B > 0 else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+
+    if stream is None:
+        stream_h = torch.cuda.current_stream(device).cuda_stream
+    elif isinstance(stream, torch.cuda.Stream):
+        stream_h = stream.cuda_stream
+    else:
+        stream_h = int(stream)
+
+    args = [_ptr(xb), _ptr(mask)] + [_ptr(params[n]) for n in _PARAM_ORDER] + \
+        [B, N, c_z, c, code, float(eps), _ptr(out_t), workspace.data_ptr(), ws_bytes, stream_h]
+    with torch.cuda.device(device):
+        if _stage is None:
+            st = lib.trimul_forward(*args)
+        else:
+            st = lib.trimul_forward_stage(int(_stage), *args)
+    raise_for_status(st, "triangle_multiplicative_update")
+    return ret
+
+
+class Prepared:
+    """A call with its tensors fixed: arguments are checked and marshalled once,
+    then ``forward()`` / ``stage(s)`` go straight to the C ABI (no per-call
+    Python checks, no allocation). The C side still validates every call.
+
+    Buffers must stay alive and unchanged in shape for the object's lifetime.
+    """
+
+    def __init__(self, x, direction, mask, params, out, workspace, eps=1e-5, stream=None):
+        code = _direction_code(direction)
+        for n in _REQUIRED:
+            if params.get(n) is None:
+                raise ValueError(f"{n} is required")
+        for n, t in [("x", x), ("out", out), ("mask", mask), *params.items()]:
+            if t is not None and (t.dtype != torch.bfloat16 or not t.is_contiguous()
+                                  or t.device != x.device):
+                raise ValueError(f"{n} must be a contiguous bf16 tensor on {x.device}")
+        xb = x.unsqueeze(0) if x.dim() == 3 else x
+        B, N, _, c_z = xb.shape
+        c = params["p_in_weight"].shape[0] // 2
+        self.device = x.device
+        self.stream = (torch.cuda.current_stream(x.device).cuda_stream if stream is None
+                       else (stream.cuda_stream if isinstance(stream, torch.cuda.Stream) else int(stream)))
+        self._keep = (x, mask, params, out, workspace)
+        self.args = tuple([_ptr(x), _ptr(mask)] + [_ptr(params.get(n)) for n in _PARAM_ORDER] +
+                          [B, N, c_z, c, code, float(eps), out.data_ptr(), workspace.data_ptr(),
+                           workspace.numel() * workspace.element_size(), self.stream])
+        st = lib.trimul_validate(*self.args[:-1])
+        raise_for_status(st, "Prepared")
+
+    def forward(self) -> None:
+        raise_for_status(lib.trimul_forward(*self.args), "forward")
+
+    def stage(self, s: int) -> None:
+        raise_for_status(lib.trimul_forward_stage(s, *self.args), f"stage {s}")

@@ -1,0 +1,124 @@
+// Device helpers shared by the three gfx950 kernels of the triangle
+// multiplicative update: bf16 packing, wave64 cross-lane sums, the two-pass
+// LayerNorm of one pair row, the logistic gate, and MFMA wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace trimul {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------- bf16 -----
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float(uint32_t(h) << 16); }
+
+// Two floats -> two bf16 (round to nearest even, v_cvt_pk_bf16_f32), lo first.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2 v = {lo, hi};
+  bf16x2 r = __builtin_convertvector(v, bf16x2);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Eight values of a 16-byte chunk, in memory order.
+__device__ __forceinline__ void unpack8(const u32x4& c, float (&v)[8]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v[2 * q] = bf16_lo(c[q]);
+    v[2 * q + 1] = bf16_hi(c[q]);
+  }
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ bf16x8 ld_frag(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// ------------------------------------------------------- cross-lane sums ---
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                              0xF, 0xF, false));
+}
+
+// Sum over each aligned group of 8 lanes. Every lane of the group ends with the
+// same bits: each step adds a lane's value to its partner's, and the two
+// partners add the same two numbers.
+__device__ __forceinline__ float sum_lanes8(float v) {
+  v = v + dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]: partner lane ^ 1
+  v = v + dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]: partner lane ^ 2
+  v = v + dpp_f<0x141>(v);  // row_half_mirror: lane i <-> 7 - i inside 8 lanes
+  return v;
+}
+
+// ------------------------------------------------------------ LayerNorm ----
+//
+// One pair row of length 64*NV is held by 8 consecutive lanes; lane `sub`
+// holds the NV chunks starting at element 8*sub + 64*v. Statistics in fp32,
+// two passes (mean, then mean of squared deviations, biased), eps inside the
+// square root, affine after normalisation, result rounded once to bf16. The
+// stage-1 and stage-3 kernels both call this with the same lane mapping, so
+// stage 3's recomputed z_in has the bits stage 1 used.
+template <int NV>
+__device__ __forceinline__ void layer_norm_row(const u32x4 (&xin)[NV], const u32x4 (&w)[NV],
+                                               const u32x4 (&b)[NV], float eps, u32x4 (&zout)[NV]) {
+#pragma clang fp contract(off)
+  constexpr float inv_n = 1.0f / float(64 * NV);
+  float v[NV][8];
+#pragma unroll
+  for (int c = 0; c < NV; ++c) unpack8(xin[c], v[c]);
+  float s = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NV; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s = s + v[c][e];
+  s = sum_lanes8(s);
+  const float mean = s * inv_n;
+  float ss = 0.0f;
+#pragma unroll
+  for (int c = 0; c < NV; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float d = v[c][e] - mean;
+      ss = __builtin_fmaf(d, d, ss);
+    }
+  ss = sum_lanes8(ss);
+  const float var = ss * inv_n;
+  const float rstd = __builtin_amdgcn_rsqf(var + eps);
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
+    float wv[8], bv[8];
+    unpack8(w[c], wv);
+    unpack8(b[c], bv);
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf((v[c][e] - mean) * rstd, wv[e], bv[e]);
+    zout[c] = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                    pack_bf16x2(o[6], o[7])};
+  }
+}
+
+// ------------------------------------------------------------- sigmoid -----
+// 1 / (1 + 2^(-g log2 e)) on the hardware exp2 and reciprocal. Saturates to 0
+// and 1 at the extremes (exp2 -> inf gives 1/inf = 0; exp2 -> 0 gives 1).
+__device__ __forceinline__ float sigmoid_f(float g) {
+  const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
+  return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// ---------------------------------------------------------------- MFMA -----
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace trimul

@@ -1,0 +1,65 @@
+// Launch interface between the C-ABI host code and the three gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace trimul {
+
+// Stage 1: LayerNorm_in + gated dual projection + mask -> planes a, b.
+struct K1Args {
+  const uint16_t* x;        // [B, N, N, c_z]
+  const uint16_t* mask;     // [B, N, N] or nullptr
+  const uint16_t* ln_w;     // [c_z]
+  const uint16_t* ln_b;     // [c_z]
+  const uint16_t* p_in;     // [2c, c_z]
+  const uint16_t* p_in_b;   // [2c] or nullptr
+  const uint16_t* g_in;     // [2c, c_z]
+  const uint16_t* g_in_b;   // [2c] or nullptr
+  uint16_t* plane_a;        // [c, B*N, n_pad]
+  uint16_t* plane_b;        // [c, B*N, n_pad]
+  int B, N, n_pad, c_z, c;
+  int incoming;
+  int nchunk;               // tiles per plane row: ceil(N / 64)
+  int ntiles;               // B * N * nchunk
+  float eps;
+};
+
+// Stage 2: per-channel contraction y(ch, r, j) = sum_k a(ch, r, k) b(ch, r', k).
+struct K2Args {
+  const uint16_t* plane_a;
+  const uint16_t* plane_b;
+  uint16_t* plane_y;
+  int B, N, n_pad, c;
+  int tiles_m, tiles_n;     // output tiles per (channel, batch) matrix
+  int nblocks;
+};
+
+// Stage 3: LayerNorm_out + LayerNorm_in recomputed + gated output projection.
+struct K3Args {
+  const uint16_t* plane_y;  // [c, B*N, n_pad]
+  const uint16_t* x;        // [B, N, N, c_z]
+  const uint16_t* ln_in_w;
+  const uint16_t* ln_in_b;
+  const uint16_t* ln_out_w;  // [c]
+  const uint16_t* ln_out_b;  // [c]
+  const uint16_t* p_out;    // [c_z, c]
+  const uint16_t* p_out_b;  // [c_z] or nullptr
+  const uint16_t* g_out;    // [c_z, c_z]
+  const uint16_t* g_out_b;  // [c_z] or nullptr
+  uint16_t* out;            // [B, N, N, c_z]
+  int B, N, n_pad, c_z, c;
+  int nchunk;
+  int ntiles;
+  float eps;
+};
+
+hipError_t launch_k1(const K1Args& a, int grid_x, hipStream_t stream);
+hipError_t launch_k2(const K2Args& a, hipStream_t stream);
+hipError_t launch_k3(const K3Args& a, int grid_x, hipStream_t stream);
+
+int k1_tiles(int B, int N);
+int k3_tiles(int B, int N);
+void k2_tiles(int N, int& tiles_m, int& tiles_n);
+
+}  // namespace trimul
