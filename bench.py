@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="time the oracle on this many output rows only (0 = the whole call)")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run --steps plain device copies of this many MiB (for scaling "
+                         "the HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -115,6 +118,15 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}), flush=True)
+        return
     name = args.workload or si.BENCH_WORKLOAD
     wl = si.WORKLOADS[name]
     direction = args.direction

@@ -73,8 +73,9 @@ const char* trimul_version(void);
 const char* trimul_last_error(void);
 
 /* The padded inner length of the channel-major planes: N rounded up to a
- * multiple of 8 (same page, "Prepared class API": the inner axis padded to a
- * multiple of 8). */
+ * multiple of 64 (same page, "Prepared class API", pads the inner axis to a
+ * multiple of 8; a multiple of 64 here lets the contraction's k steps and the
+ * 64-pair tiles of the other stages run without a tail). */
 int trimul_n_pad(int N);
 
 /* Workspace bytes for one call: three channel-major bf16 planes a, b and y,
@@ -85,8 +86,8 @@ int trimul_n_pad(int N);
  *   outgoing: a(ch, b*N+i, k) = a[b,i,k,ch]    b(ch, b*N+j, k) = b[b,j,k,ch]
  *   incoming: a(ch, b*N+i, k) = a[b,k,i,ch]    b(ch, b*N+j, k) = b[b,k,j,ch]
  *   both:     y(ch, b*N+i, j) = y[b,i,j,ch]
- * Columns s in [N, n_pad) of a and b are written as +0.0; those of y are not
- * written. Returns 0 for arguments outside the envelope. */
+ * Columns s in [N, n_pad) of a and b are written as +0.0; those of y hold
+ * unspecified values. Returns 0 for arguments outside the envelope. */
 size_t trimul_workspace_bytes(int B, int N, int c, int direction);
 
 /* Typed support check with no launch (same page, "Served today, and the typed

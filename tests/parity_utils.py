@@ -63,7 +63,7 @@ def call(dev_inp, direction, *, out=None, workspace=None, eps=1e-5, stage=None, 
 
 def planes(workspace: torch.Tensor, B: int, N: int, c: int):
     """Views of the a, b, y planes [c, B*N, n_pad] in a call's workspace."""
-    n_pad = (N + 7) // 8 * 8
+    n_pad = (N + 63) // 64 * 64
     elems = c * B * N * n_pad
     pb = (elems * 2 + 255) // 256 * 256
     out = []

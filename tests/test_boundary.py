@@ -41,7 +41,7 @@ def test_version_and_error_strings():
 
 
 def n_pad(N):
-    return (N + 7) // 8 * 8
+    return (N + 63) // 64 * 64
 
 
 @pytest.mark.parametrize("B,N,c", [(1, 64, 128), (1, 77, 128), (2, 512, 256), (1, 1536, 128), (3, 1, 128)])

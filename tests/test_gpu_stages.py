@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synthetic_inputs as si
-from parity_utils import (assert_within_tolerance, bf16_to_f64, bf16_ulp_distance, call, planes,
+from parity_utils import (assert_within_tolerance, bf16_to_f64, call, planes,
                           plane_layout, say, to_device)
 from triangle_multiplicative_update_amd import workspace_bytes
 
@@ -39,22 +39,30 @@ def test_planes_match_oracle(gpu, direction, B, N, c):
     torch.cuda.synchronize()
     ref = oracle.forward(inp, direction)
     pa, pb, py = planes(ws, B, N, c)
+    report = {}
     for name, plane, want in (("a", pa, ref.a), ("b", pb, ref.b), ("y", py, ref.y)):
         got = bf16_to_f64(plane[:, :, :N])
-        exp = plane_layout(want, direction, name)
-        ulps = bf16_ulp_distance(got, exp)
-        frac = np.count_nonzero(ulps) / ulps.size
-        say(f"[planes] {name}: mismatch fraction {frac:.2e}, max ulps {ulps.max()}")
-        # fp32 vs fp64 before the single rounding: rare one-ulp flips only
-        # (y also inherits the flips of a and b through the sum).
-        assert ulps.max() <= (1 if name != "y" else 2), name
-        assert frac <= (1e-2 if name != "y" else 0.2), name
+        exp = plane_layout(want, direction, name).astype(np.float64)
+        scale = float(np.sqrt(np.mean(exp ** 2)))
+        diff = np.abs(got - exp)
+        frac = np.count_nonzero(diff) / diff.size
+        # fp32 (GPU) vs fp64 (oracle) before the single rounding: a difference is
+        # one bf16 ulp of the value (2^-7 relative at most), or the effect of a
+        # one-ulp flip of a z_in element of the same pair (|w| * ulp(z), a few
+        # 1e-3 of the plane's scale), rare either way. y also inherits the flips
+        # of a and b through the contraction.
+        rel, floor, max_frac = (2.0 ** -7, 1e-2, 1e-2) if name != "y" else (2.0 ** -6, 1e-2, 0.2)
+        worst = float(np.max(diff - (rel * np.abs(exp) + floor * scale)))
+        report[name] = (frac, worst, max_frac)
+        say(f"[planes] {name}: mismatch fraction {frac:.2e}, worst excess {worst:.3e} (scale {scale:.3e})")
         if name != "y":
-            # padded plane columns are written as +0.0
             n_pad = plane.shape[-1]
-            if n_pad > N:
+            if n_pad > N:   # padded plane columns are written as +0.0
                 tail = plane[:, :, N:].float().cpu().numpy()
                 assert np.all(tail == 0) and not np.any(np.signbit(tail)), name
+    for name, (frac, worst, max_frac) in report.items():
+        assert worst <= 0, (name, report)
+        assert frac <= max_frac, (name, report)
     # the output itself
     assert_within_tolerance(bf16_to_f64(out), ref.out, f"{wl.name} {direction}")
 

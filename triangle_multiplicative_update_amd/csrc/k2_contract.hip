@@ -7,15 +7,24 @@
 // and numerics": y accumulated in fp32 and rounded once to bf16.
 //
 // Stage 1 writes the incoming planes with the pair index order swapped, so in
-// both directions this kernel computes Y = A * B^T on [N x n_pad] row-major
-// matrices (k contiguous in both operands): the NT form the matrix cores read
-// without any transpose.
+// both directions this kernel computes Y = A B^T on row-major [N x n_pad]
+// matrices with k contiguous in both operands: the form the matrix cores read
+// without a transpose. n_pad is a multiple of 64 and the padded columns hold
+// +0.0, so the k loop has no tail.
 //
-// Tile: 128 x 128 outputs per 256-thread block, 4 waves of 64 x 64, each a 2 x 2
-// grid of v_mfma_f32_32x32x16_bf16. K advances 32 columns per step through a
-// double-buffered LDS stage; the next step's global loads are in flight while
-// the current step multiplies. Blocks are numbered so that the blocks of one
-// (channel, batch) matrix run on one XCD and share its L2.
+// Tile: 256 x 256 outputs per block of 8 waves (2 x 4), each wave 128 (i) x
+// 64 (j) as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks. K advances 32 columns per
+// step through a 4-stage LDS ring filled by direct global->LDS loads
+// (global_load_lds_dwordx4), three steps ahead of the matrix cores, one
+// barrier per step. The ring is laid out in 256-byte lines (one line of the
+// 64 four-byte banks) holding 4 rows of 32 k each, with the 16-byte chunk
+// index XOR-ed by the line index, so the 16 lanes of a fragment read hit 16
+// distinct bank groups. Rows past N are clamped to row N-1 (their results are
+// discarded). The epilogue stages the bf16 tile in LDS and writes 512-byte
+// row segments of y. Blocks are numbered so that the tiles of one (channel,
+// batch) matrix run on one XCD and share its L2.
+
+#include <cstdlib>
 
 #include "trimul_device.hpp"
 #include "trimul_kernels.hpp"
@@ -24,23 +33,81 @@ namespace trimul {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 32;
-constexpr int K2_THREADS = 256;
-constexpr int PITCH = BK + 8;     // LDS row pitch (bf16): 80 bytes
+constexpr int K2_THREADS = 512;
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// one 16-byte-per-lane global -> LDS copy: lane l's 16 bytes land at lds + 16 l
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+
+// workgroup barrier without the memory fence of __syncthreads()
+__device__ __forceinline__ void bare_barrier() { __builtin_amdgcn_s_barrier(); }
+
+// wait until at most n vector-memory operations of this wave are outstanding
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
+// Block tile BM (i) x BN (j), k step BK, STAGES-deep ring, 8 waves as WM x WN.
+template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_>
+struct K2Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, STAGES = STAGES_, WM = WM_, WN = WN_;
+  static_assert(WM * WN == 8, "8 waves");
+  static constexpr int KC = BK / 8;              // 16-byte chunks per row per step
+  static constexpr int RPL = 16 / KC;            // rows per 256-byte LDS line
+  static constexpr int A_BYTES = BM * BK * 2;
+  static constexpr int B_BYTES = BN * BK * 2;
+  static constexpr int STAGE_BYTES = A_BYTES + B_BYTES;
+  static constexpr int RING_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int IA = A_BYTES / 1024 / 8;  // 1-KiB load instructions per wave per step
+  static constexpr int IB = B_BYTES / 1024 / 8;
+  static constexpr int PER_STEP = IA + IB;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int MI = WTM / 32, NJ = WTN / 32;
+  static constexpr int YP = BN * 2 + 16;         // epilogue row pitch (bytes)
+  static constexpr int SMEM = (BM * YP > RING_BYTES) ? BM * YP : RING_BYTES;
+  static_assert(IA * 8 * 1024 == A_BYTES && IB * 8 * 1024 == B_BYTES, "whole instructions");
+  static_assert(SMEM <= 160 * 1024, "LDS");
+
+  // Byte offset in an operand tile of the 16-byte chunk (row r, k-chunk c):
+  // 256-byte lines of RPL rows, chunk index XOR-ed by the line index.
+  __device__ __forceinline__ static int off(int r, int c) {
+    const int line = r / RPL;
+    const int q = ((r % RPL) * KC + c) ^ (line & 15);
+    return (line * 16 + q) * 16;
+  }
+  // inverse: the (row, chunk) that lands on chunk P of a tile
+  __device__ __forceinline__ static void src(int P, int& r, int& c) {
+    const int line = P >> 4;
+    const int x = (P & 15) ^ (line & 15);
+    r = line * RPL + x / KC;
+    c = x % KC;
+  }
+};
+
+}  // namespace
+
+// (kept outside the unnamed namespace: the host stubs of template kernels
+// must have external linkage to be emitted for every instantiation)
+template <int BM, int BN, int BK, int STAGES, int WM, int WN>
 __global__ __launch_bounds__(K2_THREADS) void k2_contract(const K2Args p) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][BM * PITCH];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN * PITCH];
+  using C = K2Cfg<BM, BN, BK, STAGES, WM, WN>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = uniform(tid >> 6);
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / C::WN;
+  const int wn = wave % C::WN;
 
-  // XCD-aware numbering: hardware block id b runs on XCD b % 8; give XCD x the
-  // contiguous logical range [x * n / 8, (x + 1) * n / 8).
   int logical = blockIdx.x;
   const int nb = p.nblocks;
   if ((nb & 7) == 0) logical = (blockIdx.x & 7) * (nb >> 3) + (blockIdx.x >> 3);
@@ -50,97 +117,174 @@ __global__ __launch_bounds__(K2_THREADS) void k2_contract(const K2Args p) {
   const int tm = tile / p.tiles_n;
   const int tn = tile - tm * p.tiles_n;
   const int N = p.N, ld = p.n_pad;
-  const int i0 = tm * BM, j0 = tn * BN;
-  const size_t base = size_t(mat) * N * ld;   // rows (ch, b, 0..N-1)
+  const int i0 = tm * C::BM, j0 = tn * C::BN;
+  const size_t base = size_t(mat) * N * ld;
   const uint16_t* Ag = p.plane_a + base;
   const uint16_t* Bg = p.plane_b + base;
 
-  // global -> register staging: 2 chunks of A and 2 of B per thread
-  u32x4 ra[2], rb[2];
-  auto load = [&](int k0) {
+  // this lane's load sources (rows past N clamp to N - 1)
+  const uint16_t* srcA[C::IA];
+  const uint16_t* srcB[C::IB];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int id = tid + h * K2_THREADS;
-      const int r = id >> 2;
-      const int kc = k0 + 8 * (id & 3);
-      const bool kin = kc < ld;
-      ra[h] = (kin && i0 + r < N) ? ld16(Ag + size_t(i0 + r) * ld + kc) : u32x4{0, 0, 0, 0};
-      rb[h] = (kin && j0 + r < N) ? ld16(Bg + size_t(j0 + r) * ld + kc) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store = [&](int buf) {
+  for (int t = 0; t < C::IA; ++t) {
+    int r, c;
+    C::src((wave * C::IA + t) * 64 + lane, r, c);
+    srcA[t] = Ag + size_t(min(i0 + r, N - 1)) * ld + 8 * c;
+  }
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int id = tid + h * K2_THREADS;
-      const int r = id >> 2;
-      const int kk = 8 * (id & 3);
-      st16(&As[buf][r * PITCH + kk], ra[h]);
-      st16(&Bs[buf][r * PITCH + kk], rb[h]);
-    }
+  for (int t = 0; t < C::IB; ++t) {
+    int r, c;
+    C::src((wave * C::IB + t) * 64 + lane, r, c);
+    srcB[t] = Bg + size_t(min(j0 + r, N - 1)) * ld + 8 * c;
+  }
+  auto issue = [&](int step) {
+    uint8_t* st = smem + (step % C::STAGES) * C::STAGE_BYTES;
+    const int k0 = step * C::BK;
+#pragma unroll
+    for (int t = 0; t < C::IA; ++t)
+      load_lds16(srcA[t] + k0, st + (wave * C::IA + t) * 1024);
+#pragma unroll
+    for (int t = 0; t < C::IB; ++t)
+      load_lds16(srcB[t] + k0, st + C::A_BYTES + (wave * C::IB + t) * 1024);
   };
 
-  f32x16 acc[2][2];
+  constexpr int SUB = C::BK / 16;
+  int offA[C::MI][SUB], offB[C::NJ][SUB];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi)
+  for (int s = 0; s < SUB; ++s) {
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni)
+    for (int mi = 0; mi < C::MI; ++mi) offA[mi][s] = C::off(wm * C::WTM + 32 * mi + l32, 2 * s + lhi);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[mi][ni][r] = 0.0f;
-
-  const int nk = (ld + BK - 1) / BK;
-  load(0);
-  store(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) load((kt + 1) * BK);
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 16) {
-      bf16x8 af[2], bfr[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        af[mi] = ld_frag(&As[buf][(wm * 64 + 32 * mi + l32) * PITCH + kk + 8 * lhi]);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        bfr[ni] = ld_frag(&Bs[buf][(wn * 64 + 32 * ni + l32) * PITCH + kk + 8 * lhi]);
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni) acc[mi][ni] = mfma32x32x16(af[mi], bfr[ni], acc[mi][ni]);
-    }
-    if (kt + 1 < nk) store(buf ^ 1);
-    __syncthreads();
+    for (int nj = 0; nj < C::NJ; ++nj) offB[nj][s] = C::A_BYTES + C::off(wn * C::WTN + 32 * nj + l32, 2 * s + lhi);
   }
 
-  // epilogue: D[m = i][n = j]; lane holds column j = l32, rows 8*(r/4) + 4*lhi + r%4
-  uint16_t* Y = p.plane_y + base;
+  f32x16 acc[C::MI][C::NJ];
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+  for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 2; ++ni) {
-      const int j = j0 + wn * 64 + 32 * ni + l32;
-      if (j < N) {
+    for (int nj = 0; nj < C::NJ; ++nj)
 #pragma unroll
-        for (int r = 0; r < 16; r += 2) {
-          const int i = i0 + wm * 64 + 32 * mi + 8 * (r >> 2) + 4 * lhi + (r & 3);
-          const uint32_t w = pack_bf16x2(acc[mi][ni][r], acc[mi][ni][r + 1]);
-          if (i < N) Y[size_t(i) * ld + j] = uint16_t(w & 0xffffu);
-          if (i + 1 < N) Y[size_t(i + 1) * ld + j] = uint16_t(w >> 16);
-        }
+      for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
+
+  const int nk = ld / C::BK;
+#pragma unroll
+  for (int s = 0; s < C::STAGES - 1; ++s)
+    if (s < nk) issue(s);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // step kt's loads are done once at most those of the later issued steps remain
+    const int later = min(C::STAGES - 2, nk - 1 - kt);
+    if (later >= 3) wait_vm<3 * C::PER_STEP>();
+    else if (later == 2) wait_vm<2 * C::PER_STEP>();
+    else if (later == 1) wait_vm<C::PER_STEP>();
+    else wait_vm<0>();
+    // a bare barrier: __syncthreads() would also drain the loads in flight
+    // for the later steps
+    bare_barrier();
+    if (kt + C::STAGES - 1 < nk) issue(kt + C::STAGES - 1);
+
+    const uint8_t* st = smem + (kt % C::STAGES) * C::STAGE_BYTES;
+#pragma unroll
+    for (int s = 0; s < SUB; ++s) {
+      bf16x8 af[C::MI], bfr[C::NJ];
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi) af[mi] = ld_frag(st + offA[mi][s]);
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = ld_frag(st + offB[nj][s]);
+      // D[j][i]: rows from plane b, columns from plane a, so each lane ends
+      // with 4 consecutive j of one i (8 contiguous bytes of a y row)
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+        for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = mfma32x32x16(bfr[nj], af[mi], acc[mi][nj]);
+    }
+  }
+  __syncthreads();   // the ring is reused as the epilogue staging area
+
+  // ---- epilogue: bf16 tile in LDS [i][j], then 16-byte row stores ----
+#pragma unroll
+  for (int mi = 0; mi < C::MI; ++mi) {
+    const int ii = wm * C::WTM + 32 * mi + l32;
+#pragma unroll
+    for (int nj = 0; nj < C::NJ; ++nj) {
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const int jj = wn * C::WTN + 32 * nj + 8 * rg + 4 * lhi;
+        const u32x2 w = {pack_bf16x2(acc[mi][nj][4 * rg], acc[mi][nj][4 * rg + 1]),
+                         pack_bf16x2(acc[mi][nj][4 * rg + 2], acc[mi][nj][4 * rg + 3])};
+        *reinterpret_cast<u32x2*>(smem + ii * C::YP + jj * 2) = w;
       }
     }
   }
+  __syncthreads();
+  uint16_t* Y = p.plane_y + base;
+  const int jrem = min(C::BN, ld - j0);       // columns inside this row (n_pad bound)
+  constexpr int CPR = C::BN / 8;              // 16-byte chunks per tile row
+#pragma unroll 4
+  for (int it = 0; it < (C::BM * CPR) / K2_THREADS; ++it) {
+    const int id = it * K2_THREADS + tid;
+    const int ii = id / CPR;
+    const int cc = id % CPR;
+    if (i0 + ii < N && 8 * cc < jrem)
+      st16(Y + size_t(i0 + ii) * ld + j0 + 8 * cc, ld16(smem + ii * C::YP + cc * 16));
+  }
+}
+
+// explicit instantiations of every configuration's kernel (and its host stub)
+template __global__ void k2_contract<256, 256, 32, 4, 2, 4>(const K2Args);
+template __global__ void k2_contract<256, 128, 64, 3, 4, 2>(const K2Args);
+template __global__ void k2_contract<256, 256, 64, 2, 2, 4>(const K2Args);
+template __global__ void k2_contract<128, 256, 64, 3, 2, 4>(const K2Args);
+
+namespace {
+
+// The tile configurations (see k2_config below).
+using CfgSq32 = K2Cfg<256, 256, 32, 4, 2, 4>;   // 256 x 256, k 32, 4 stages
+using CfgRect64 = K2Cfg<256, 128, 64, 3, 4, 2>; // 256 x 128, k 64, 3 stages
+using CfgSq64 = K2Cfg<256, 256, 64, 2, 2, 4>;   // 256 x 256, k 64, 2 stages
+using CfgTall64 = K2Cfg<128, 256, 64, 3, 2, 4>; // 128 x 256, k 64, 3 stages
+
+int g_cfg = -1;   // chosen once per process
+
+int k2_config() {
+  if (g_cfg < 0) {
+    int c = 1;
+    if (const char* e = std::getenv("TRIMUL_K2_TILE")) c = std::atoi(e);
+    g_cfg = (c >= 0 && c <= 3) ? c : 1;
+  }
+  return g_cfg;
+}
+
+template <class C>
+void tiles_of(int N, int& tm, int& tn) {
+  tm = (N + C::BM - 1) / C::BM;
+  tn = (N + C::BN - 1) / C::BN;
 }
 
 }  // namespace
 
 void k2_tiles(int N, int& tiles_m, int& tiles_n) {
-  tiles_m = (N + BM - 1) / BM;
-  tiles_n = (N + BN - 1) / BN;
+  switch (k2_config()) {
+    case 0: tiles_of<CfgSq32>(N, tiles_m, tiles_n); break;
+    case 2: tiles_of<CfgSq64>(N, tiles_m, tiles_n); break;
+    case 3: tiles_of<CfgTall64>(N, tiles_m, tiles_n); break;
+    default: tiles_of<CfgRect64>(N, tiles_m, tiles_n); break;
+  }
+}
+
+template <class C>
+void launch_cfg(const K2Args& a, hipStream_t stream) {
+  hipLaunchKernelGGL((k2_contract<C::BM, C::BN, C::BK, C::STAGES, C::WM, C::WN>), dim3(a.nblocks),
+                     dim3(K2_THREADS), 0, stream, a);
 }
 
 hipError_t launch_k2(const K2Args& a, hipStream_t stream) {
-  hipLaunchKernelGGL(k2_contract, dim3(a.nblocks), dim3(K2_THREADS), 0, stream, a);
+  switch (k2_config()) {
+    case 0: launch_cfg<CfgSq32>(a, stream); break;
+    case 2: launch_cfg<CfgSq64>(a, stream); break;
+    case 3: launch_cfg<CfgTall64>(a, stream); break;
+    default: launch_cfg<CfgRect64>(a, stream); break;
+  }
   return hipGetLastError();
 }
 

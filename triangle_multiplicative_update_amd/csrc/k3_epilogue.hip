@@ -8,18 +8,18 @@
 // operands, out rounded once to bf16, not masked. Section "Overview": y arrives
 // channel-major, out leaves pair-major.
 //
-// Work decomposition. A tile is 64 pairs (b, i, j0..j0+63): one row of each y
-// plane (128 contiguous bytes per channel) and 64 contiguous pair rows of x
-// and out. A persistent block of 8 waves keeps the output weights in registers:
-// each wave owns 32 output channels (p_out and g_out rows) and one or both
-// 32-pair halves of the tile.
+// Work decomposition. A tile is 64 pairs (b, i, j0..j0+63): one 128-byte row
+// of each y plane and 64 contiguous pair rows of x and out. A persistent
+// block of 8 waves keeps the output weights in registers: each wave owns 32
+// output channels (p_out and g_out rows) and one or both 32-pair halves.
 //
-// Per tile: y (c channels x 64 pairs) -> LDS transposed to [pair][channel];
-// x -> registers -> LayerNorm_in (the stage-1 lane mapping, so z_in is
-// bit-identical) -> LDS; LayerNorm_out in place on the y rows; MFMA 32x32x16 with
-// D[out channel][pair] (A = weights, B = activations) for the value and the gate;
-// sigmoid * value in fp32 -> bf16 -> LDS [pair][channel] -> 16-byte coalesced
-// stores of out.
+// Per tile: y (c channels x 64 pairs, prefetched one tile ahead) is
+// transposed to pair-major LDS rows by packing two channels per dword; x
+// (prefetched) -> LayerNorm_in with the stage-1 lane mapping, so z_in is
+// bit-identical -> LDS; LayerNorm_out in place on the y rows; MFMA 32x32x16
+// with D[out channel][pair] for the value and the gate; sigmoid * value in
+// fp32 -> bf16 -> LDS [pair][channel] -> 16-byte coalesced stores of out.
+// All pair-major LDS tiles use the 256-byte-row slot swizzle (lds_swz).
 
 #include "trimul_device.hpp"
 #include "trimul_kernels.hpp"
@@ -33,19 +33,26 @@ constexpr int K3_TP = 64;
 
 template <int C>
 struct K3Smem {
-  static constexpr int P = C + 8;          // row pitch (bf16) of the pair-major tiles
-  uint16_t y[K3_TP * P];                   // y, then u, [pair][channel]
-  uint16_t z[K3_TP * P];                   // z_in [pair][channel]
-  uint16_t o[K3_TP * P];                   // out staging [pair][channel]
+  static constexpr int RB = C * 2;         // row bytes (pair-major, no padding)
+  uint8_t y[K3_TP * RB];                   // y, then u
+  uint8_t z[K3_TP * RB];                   // z_in
+  uint8_t o[K3_TP * RB];                   // out staging
 };
+
+// byte offset of 16-byte slot `slot` of pair row `r` in a swizzled tile
+template <int C>
+__device__ __forceinline__ int soff(int r, int slot) {
+  return r * (C * 2) + ((slot ^ lds_swz(r)) << 4);
+}
 
 template <int C>
 __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   constexpr int CZ = C;                    // c_z == c
-  constexpr int NV = C / 64;
-  constexpr int KS = C / 16;
+  constexpr int NV = C / 64;               // LayerNorm chunks per lane
+  constexpr int KS = C / 16;               // MFMA k-steps
   constexpr int NB = CZ / 32;              // 32-channel output blocks
   constexpr int JOBS = 2 * NB / 8;         // (channel block, pair half) jobs per wave
+  constexpr int NY = (C / 2) * 8 / K3_THREADS;   // (channel pair, 8-pair chunk) items per thread
   using S = K3Smem<C>;
   __shared__ __attribute__((aligned(16))) S sm;
 
@@ -74,7 +81,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
     bias_g[r] = p.g_out_b ? bf16_to_f32(p.g_out_b[n]) : 0.0f;
   }
 
-  // ---- LayerNorm lane mapping (same as stage 1) ----
+  // ---- LayerNorm lane mapping (same as stage 1): pair lp, sub-lane sub ----
   const int lp = tid >> 3;
   const int sub = tid & 7;
   u32x4 inw[NV], inb[NV], outw[NV], outb[NV];
@@ -89,52 +96,75 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   const int N = p.N;
   const size_t ch_stride = size_t(p.B) * N * p.n_pad;
 
-  for (int t = blockIdx.x; t < p.ntiles; t += gridDim.x) {
+  // ---- register prefetch of one tile: y (channel pairs) and x ----
+  u32x4 ya[NY], yb[NY], xr[NV];
+  auto prefetch = [&](int t) {
+    const int row = t / p.nchunk;
+    const int j0 = (t - row * p.nchunk) * K3_TP;
+    // y item: channel pair cp = id / 8, pair chunk jc = id % 8 (8 lanes cover one
+    // channel's 128 bytes)
+#pragma unroll
+    for (int it = 0; it < NY; ++it) {
+      const int id = it * K3_THREADS + tid;
+      const int cp = id >> 3;
+      const int jc = id & 7;
+      const uint16_t* src = p.plane_y + size_t(2 * cp) * ch_stride + size_t(row) * p.n_pad + j0 + 8 * jc;
+      ya[it] = ld16(src);
+      yb[it] = ld16(src + ch_stride);
+    }
+    const bool valid = j0 + lp < N;
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+      xr[v] = valid ? ld16(p.x + (size_t(row) * N + j0 + lp) * CZ + 8 * sub + 64 * v) : u32x4{0, 0, 0, 0};
+  };
+
+  int t = blockIdx.x;
+  if (t < p.ntiles) prefetch(t);
+  for (; t < p.ntiles; t += gridDim.x) {
     const int row = t / p.nchunk;                      // b * N + i
     const int j0 = (t - row * p.nchunk) * K3_TP;
 
-    // ---- y rows of the tile -> LDS, transposed to [pair][channel] ----
+    // ---- y -> pair-major LDS rows (two channels per dword) ----
 #pragma unroll
-    for (int it = 0; it < (C * K3_TP / 8) / K3_THREADS; ++it) {
+    for (int it = 0; it < NY; ++it) {
       const int id = it * K3_THREADS + tid;
-      const int ch = id >> 3;
+      const int cp = id >> 3;
       const int jc = id & 7;
-      const int col = j0 + 8 * jc;
-      u32x4 v = u32x4{0, 0, 0, 0};
-      if (col < p.n_pad) v = ld16(p.plane_y + size_t(ch) * ch_stride + size_t(row) * p.n_pad + col);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        sm.y[(8 * jc + 2 * q) * S::P + ch] = uint16_t(v[q] & 0xffffu);
-        sm.y[(8 * jc + 2 * q + 1) * S::P + ch] = uint16_t(v[q] >> 16);
+        const uint32_t a = ya[it][q], b = yb[it][q];
+        const uint32_t even = (a & 0xffffu) | (b << 16);          // pair 8jc + 2q
+        const uint32_t odd = (a >> 16) | (b & 0xffff0000u);       // pair 8jc + 2q + 1
+        const int r0 = 8 * jc + 2 * q;
+        *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0, cp >> 2) + 4 * (cp & 3)) = even;
+        *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0 + 1, cp >> 2) + 4 * (cp & 3)) = odd;
       }
     }
-
     // ---- x -> LayerNorm_in -> z_in in LDS ----
     {
-      const bool valid = j0 + lp < N;
-      u32x4 xr[NV], z[NV];
-#pragma unroll
-      for (int v = 0; v < NV; ++v)
-        xr[v] = valid ? ld16(p.x + (size_t(row) * N + j0 + lp) * CZ + 8 * sub + 64 * v) : u32x4{0, 0, 0, 0};
-      if (valid) {
+      u32x4 z[NV];
+      if (j0 + lp < N) {
         layer_norm_row<NV>(xr, inw, inb, p.eps, z);
       } else {
 #pragma unroll
         for (int v = 0; v < NV; ++v) z[v] = u32x4{0, 0, 0, 0};
       }
 #pragma unroll
-      for (int v = 0; v < NV; ++v) st16(&sm.z[lp * S::P + 8 * sub + 64 * v], z[v]);
+      for (int v = 0; v < NV; ++v) st16(sm.z + soff<C>(lp, sub + 8 * v), z[v]);
     }
     __syncthreads();
+
+    // ---- prefetch the next tile while this one is processed ----
+    if (t + gridDim.x < p.ntiles) prefetch(t + gridDim.x);
 
     // ---- LayerNorm_out in place on the pair rows of y ----
     {
       u32x4 yr[NV], u[NV];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) yr[v] = ld16(&sm.y[lp * S::P + 8 * sub + 64 * v]);
+      for (int v = 0; v < NV; ++v) yr[v] = ld16(sm.y + soff<C>(lp, sub + 8 * v));
       layer_norm_row<NV>(yr, outw, outb, p.eps, u);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) st16(&sm.y[lp * S::P + 8 * sub + 64 * v], u[v]);
+      for (int v = 0; v < NV; ++v) st16(sm.y + soff<C>(lp, sub + 8 * v), u[v]);
     }
     __syncthreads();
 
@@ -151,8 +181,8 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
       const int prow = 32 * mb + l32;     // pair this lane feeds as the B operand
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const bf16x8 u = ld_frag(&sm.y[prow * S::P + 16 * ks + 8 * lhi]);
-        const bf16x8 z = ld_frag(&sm.z[prow * S::P + 16 * ks + 8 * lhi]);
+        const bf16x8 u = ld_frag(sm.y + soff<C>(prow, 2 * ks + lhi));
+        const bf16x8 z = ld_frag(sm.z + soff<C>(prow, 2 * ks + lhi));
         acc_p = mfma32x32x16(wp[ks], u, acc_p);
         acc_g = mfma32x32x16(wg[ks], z, acc_g);
       }
@@ -163,7 +193,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) o[q] = sigmoid_f(acc_g[4 * rg + q]) * acc_p[4 * rg + q];
         const u32x2 packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        *reinterpret_cast<u32x2*>(&sm.o[prow * S::P + 32 * nb + 8 * rg + 4 * lhi]) = packed;
+        *reinterpret_cast<u32x2*>(sm.o + soff<C>(prow, 4 * nb + rg) + 8 * lhi) = packed;
       }
     }
     __syncthreads();
@@ -175,7 +205,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
       const int pr = id / (CZ / 8);
       const int cc = id - pr * (CZ / 8);
       if (j0 + pr < N)
-        st16(p.out + (size_t(row) * N + j0 + pr) * CZ + 8 * cc, ld16(&sm.o[pr * S::P + 8 * cc]));
+        st16(p.out + (size_t(row) * N + j0 + pr) * CZ + 8 * cc, ld16(sm.o + soff<C>(pr, cc)));
     }
   }
 }

@@ -40,7 +40,7 @@ int ok() {
 
 constexpr long long kLimit = 1LL << 31;
 
-long long n_pad_of(long long N) { return (N + 7) / 8 * 8; }
+long long n_pad_of(long long N) { return (N + 63) / 64 * 64; }
 
 size_t plane_bytes(int B, int N, int c) {
   const size_t e = size_t(c) * size_t(B) * size_t(N) * size_t(n_pad_of(N));

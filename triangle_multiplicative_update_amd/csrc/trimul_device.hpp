@@ -60,6 +60,19 @@ __device__ __forceinline__ float sum_lanes8(float v) {
   return v;
 }
 
+// ------------------------------------------------------- LDS swizzle ----
+//
+// Pair-major LDS tiles use rows of 256 B per 128 channels (no padding) and
+// place the 16-byte slot `s` of row `r` at slot s ^ lds_swz(r). With 64
+// four-byte banks (one 256-byte line per bank cycle) this keeps three access
+// patterns free of bank conflicts: 16 consecutive rows read at one slot (MFMA
+// fragments), 2 rows x 8 slots read as 16-byte vectors (LayerNorm lanes), and
+// the transposing dword writes of 8 rows {8j + e} x 8 consecutive dwords.
+__device__ __forceinline__ int lds_swz(int r) {
+  return (((r >> 0) & 1) << 3) ^ ((r >> 1) & 1) ^ (((r >> 2) & 1) << 2) ^ (((r >> 3) & 1) << 1) ^
+         (((r >> 4) & 1) << 2) ^ (((r >> 5) & 1) << 3);
+}
+
 // ------------------------------------------------------------ LayerNorm ----
 //
 // One pair row of length 64*NV is held by 8 consecutive lanes; lane `sub`
