@@ -16,11 +16,13 @@
 // channels' value and gate weight rows (2 x 32 x c_z bf16) in registers for
 // the whole kernel, so the weights are read once per block, not per tile.
 //
-// Per tile: x (64 pairs x c_z) -> registers (prefetched one tile ahead) ->
-// LayerNorm (8 lanes per pair) -> z in LDS -> MFMA 32x32x16 (M = pairs,
-// N = channels, K = c_z) with value and gate accumulators side by side ->
-// sigmoid * value * mask in fp32 -> bf16 -> LDS transpose to [channel][pair]
-// -> 16-byte coalesced plane stores.
+// Software pipeline, one barrier per tile: the block stores tile t-1's staged
+// channel-major outputs with 16-byte coalesced writes, then -- while the
+// matrix cores multiply tile t (MFMA 32x32x16, M = pairs, N = channels, K =
+// c_z, value and gate accumulators side by side) and the VALU applies
+// sigmoid * value * mask -- runs LayerNorm of tile t+1 into the other z
+// buffer and issues the x loads of tile t+2. z, mask and output staging are
+// double-buffered in LDS.
 
 #include "trimul_device.hpp"
 #include "trimul_kernels.hpp"
@@ -30,6 +32,9 @@ namespace trimul {
 namespace {
 
 constexpr int K1_THREADS = 512;
+
+// bf16 1.0: the mask value read (at index 0) when the call has no mask
+__device__ const uint16_t kMaskOne[1] = {0x3F80};
 constexpr int K1_TP = 64;          // pairs per tile
 constexpr int K1_GROUP = 128;      // channels of a (and of b) per block
 
@@ -37,9 +42,9 @@ template <int CZ>
 struct K1Smem {
   static constexpr int ZP = CZ + 8;        // z row pitch (bf16 elements)
   static constexpr int OP = K1_TP + 8;     // staging row pitch
-  uint16_t z[K1_TP * ZP];
-  uint16_t o[2 * K1_GROUP * OP];
-  float m[K1_TP];
+  uint16_t z[2][K1_TP * ZP];
+  uint16_t o[2][2 * K1_GROUP * OP];
+  float m[2][K1_TP];
 };
 
 template <int CZ>
@@ -81,61 +86,49 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
   }
 
   const int N = p.N;
+  const int nchunk = p.nchunk;
+  const int ntiles = p.ntiles;
   const int stride = gridDim.x;
-  const size_t plane_elems = size_t(p.c) * p.B * N * p.n_pad;
   const size_t ch_stride = size_t(p.B) * N * p.n_pad;
+  // no mask: every pair reads the constant 1.0 (index stride 0), so the mask
+  // load needs no branch (a branch would force a wait on all memory traffic)
+  const uint16_t* mask = p.mask ? p.mask : kMaskOne;
+  const int mask_step = p.mask ? 1 : 0;
 
-  // x / mask element offset of the pair in slot `slot` of tile `t`.
-  auto pair_index = [&](int t, int slot, int& row, int& inner) -> int {
-    row = t / p.nchunk;
-    inner = (t - row * p.nchunk) * K1_TP + slot;
+  // x and mask of this lane's LayerNorm pair in tile t; pairs past N read a
+  // valid pair and are then zeroed (mask 0), so no branch is needed.
+  u32x4 xr[NV];
+  float mr = 0.0f;
+  auto fetch = [&](int t) {
+    const int row = t / nchunk;
+    const int inner = (t - row * nchunk) * K1_TP + lp;
+    const bool ok = inner < N;
+    const int in_c = ok ? inner : N - 1;
     const int bb = row / N;
     const int fixed = row - bb * N;
     // outgoing: pair (b, fixed, inner); incoming: pair (b, inner, fixed)
-    return p.incoming ? (bb * N + inner) * N + fixed : row * N + inner;
+    const int pi = p.incoming ? (bb * N + in_c) * N + fixed : row * N + in_c;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const u32x4 x = ld16(p.x + size_t(pi) * CZ + 8 * sub + 64 * v);
+      xr[v] = ok ? x : u32x4{0, 0, 0, 0};
+    }
+    const float m = bf16_to_f32(mask[pi * mask_step]);
+    mr = ok ? m : 0.0f;
   };
 
-  u32x4 xr[NV];
-  float mr = 0.0f;
-  auto prefetch = [&](int t) {
-    int row, inner;
-    const int pi = pair_index(t, lp, row, inner);
-    if (inner < N) {
+  // LayerNorm_in of the fetched tile -> z (bf16) and mask in LDS buffer `buf`
+  auto ln_store = [&](int buf) {
+    u32x4 z[NV];
+    layer_norm_row<NV>(xr, lnw, lnb, p.eps, z);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) xr[v] = ld16(p.x + size_t(pi) * CZ + 8 * sub + 64 * v);
-      mr = p.mask ? bf16_to_f32(p.mask[pi]) : 1.0f;
-    } else {
-#pragma unroll
-      for (int v = 0; v < NV; ++v) xr[v] = u32x4{0, 0, 0, 0};
-      mr = 0.0f;
-    }
+    for (int v = 0; v < NV; ++v) st16(&sm.z[buf][lp * S::ZP + 8 * sub + 64 * v], z[v]);
+    sm.m[buf][lp] = mr;       // the 8 lanes of a pair write the same value
   };
 
-  int t = blockIdx.x;
-  if (t < p.ntiles) prefetch(t);
-  for (; t < p.ntiles; t += stride) {
-    int row, inner0;
-    pair_index(t, 0, row, inner0);
-
-    // ---- LayerNorm_in -> z (bf16) in LDS ----
-    {
-      u32x4 z[NV];
-      if (inner0 + lp < N) {
-        layer_norm_row<NV>(xr, lnw, lnb, p.eps, z);
-      } else {
-#pragma unroll
-        for (int v = 0; v < NV; ++v) z[v] = u32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int v = 0; v < NV; ++v) st16(&sm.z[lp * S::ZP + 8 * sub + 64 * v], z[v]);
-      if (sub == 0) sm.m[lp] = mr;
-    }
-    __syncthreads();
-
-    // ---- prefetch the next tile while the matrix cores work ----
-    if (t + stride < p.ntiles) prefetch(t + stride);
-
-    // ---- projections: D[pair][channel] for value and gate ----
+  // projections of the tile in z buffer `buf`, gate * value * mask, bf16,
+  // staged channel-major in output buffer `buf`
+  auto mma_epi = [&](int buf) {
     f32x16 acc_v[2], acc_g[2];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -149,46 +142,90 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a = ld_frag(&sm.z[(32 * mb + l32) * S::ZP + 16 * ks + 8 * lhi]);
+        const bf16x8 a = ld_frag(&sm.z[buf][(32 * mb + l32) * S::ZP + 16 * ks + 8 * lhi]);
         acc_v[mb] = mfma32x32x16(a, wv[ks], acc_v[mb]);
         acc_g[mb] = mfma32x32x16(a, wg[ks], acc_g[mb]);
       }
     }
-
-    // ---- gate * value * mask, bf16, staged channel-major in LDS ----
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
         const int m0 = 32 * mb + 8 * rg + 4 * lhi;   // first of 4 consecutive pairs
+        const f32x4 mm = *reinterpret_cast<const f32x4*>(&sm.m[buf][m0]);
         float o[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = 4 * rg + q;
-          o[q] = sigmoid_f(acc_g[mb][r]) * acc_v[mb][r] * sm.m[m0 + q] + 0.0f;
+          o[q] = sigmoid_f(acc_g[mb][r]) * acc_v[mb][r] * mm[q] + 0.0f;
         }
         const u32x2 packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        *reinterpret_cast<u32x2*>(&sm.o[(plane * K1_GROUP + chs + l32) * S::OP + m0]) = packed;
+        *reinterpret_cast<u32x2*>(&sm.o[buf][(plane * K1_GROUP + chs + l32) * S::OP + m0]) = packed;
       }
     }
-    __syncthreads();
+  };
 
-    // ---- coalesced plane stores: 256 rows (128 a + 128 b) x 64 pairs ----
+  // coalesced plane stores of tile t from output buffer `buf`: 256 rows
+  // (128 a + 128 b channels) x 64 pairs; n_pad is a multiple of 64, so every
+  // 16-byte chunk of the tile lies inside its row
+  auto store = [&](int t, int buf) {
+    const int row = t / nchunk;
+    const int inner0 = (t - row * nchunk) * K1_TP;
 #pragma unroll
     for (int it = 0; it < (2 * K1_GROUP * K1_TP / 8) / K1_THREADS; ++it) {
       const int id = it * K1_THREADS + tid;
       const int srow = id >> 3;              // staging row: plane * 128 + channel
       const int c16 = id & 7;
-      const int col = inner0 + 8 * c16;
-      if (col < p.n_pad) {
-        const int pl = srow / K1_GROUP;
-        const int gch = group * K1_GROUP + (srow - pl * K1_GROUP);
-        uint16_t* dst = (pl ? p.plane_b : p.plane_a) + size_t(gch) * ch_stride + size_t(row) * p.n_pad + col;
-        st16(dst, ld16(&sm.o[srow * S::OP + 8 * c16]));
-      }
+      const int pl = srow / K1_GROUP;
+      const int gch = group * K1_GROUP + (srow - pl * K1_GROUP);
+      uint16_t* dst = (pl ? p.plane_b : p.plane_a) + size_t(gch) * ch_stride + size_t(row) * p.n_pad +
+                      inner0 + 8 * c16;
+      st16(dst, ld16(&sm.o[buf][srow * S::OP + 8 * c16]));
     }
+  };
+
+  int t = blockIdx.x;
+  if (t >= ntiles) return;
+  // prologue: LayerNorm of the first tile, x of the second in flight
+  fetch(t);
+  ln_store(0);
+  if (t + stride < ntiles) fetch(t + stride);
+  lds_barrier();
+
+  // first tile (nothing staged for storing yet)
+  int k = 0;
+  {
+    mma_epi(0);
+    if (t + stride < ntiles) {
+      ln_store(1);
+      if (t + 2 * stride < ntiles) fetch(t + 2 * stride);
+    }
+    lds_barrier();
+    t += stride;
+    k = 1;
   }
-  (void)plane_elems;
+  // Steady state: every part unconditional, one basic block per tile. The
+  // stores of tile t-1 go first: with stores and loads both in flight the
+  // memory counter only supports waiting for all of them, and the first use
+  // of the prefetched x (LayerNorm of tile t+1) comes after the whole
+  // multiply phase, by which time the stores have long completed.
+  for (; t + 2 * stride < ntiles; t += stride, ++k) {
+    const int cur = k & 1;
+    store(t - stride, cur ^ 1);
+    mma_epi(cur);
+    ln_store(cur ^ 1);
+    fetch(t + 2 * stride);
+    lds_barrier();
+  }
+  // the last (at most two) tiles
+  for (; t < ntiles; t += stride, ++k) {
+    const int cur = k & 1;
+    store(t - stride, cur ^ 1);
+    mma_epi(cur);
+    if (t + stride < ntiles) ln_store(cur ^ 1);
+    lds_barrier();
+  }
+  store(t - stride, (k - 1) & 1);
 }
 
 }  // namespace

@@ -44,9 +44,6 @@ __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
 }
 
-// workgroup barrier without the memory fence of __syncthreads()
-__device__ __forceinline__ void bare_barrier() { __builtin_amdgcn_s_barrier(); }
-
 // wait until at most n vector-memory operations of this wave are outstanding
 template <int n>
 __device__ __forceinline__ void wait_vm() {
@@ -178,9 +175,9 @@ __global__ __launch_bounds__(K2_THREADS) void k2_contract(const K2Args p) {
     else if (later == 2) wait_vm<2 * C::PER_STEP>();
     else if (later == 1) wait_vm<C::PER_STEP>();
     else wait_vm<0>();
-    // a bare barrier: __syncthreads() would also drain the loads in flight
-    // for the later steps
-    bare_barrier();
+    // an LDS-only barrier: __syncthreads() would also drain the loads in
+    // flight for the later steps
+    lds_barrier();
     if (kt + C::STAGES - 1 < nk) issue(kt + C::STAGES - 1);
 
     const uint8_t* st = smem + (kt % C::STAGES) * C::STAGE_BYTES;
@@ -199,7 +196,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_contract(const K2Args p) {
         for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = mfma32x32x16(bfr[nj], af[mi], acc[mi][nj]);
     }
   }
-  __syncthreads();   // the ring is reused as the epilogue staging area
+  lds_barrier();   // the ring is reused as the epilogue staging area
 
   // ---- epilogue: bf16 tile in LDS [i][j], then 16-byte row stores ----
 #pragma unroll
@@ -216,7 +213,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_contract(const K2Args p) {
       }
     }
   }
-  __syncthreads();
+  lds_barrier();
   uint16_t* Y = p.plane_y + base;
   const int jrem = min(C::BN, ld - j0);       // columns inside this row (n_pad bound)
   constexpr int CPR = C::BN / 8;              // 16-byte chunks per tile row
@@ -248,9 +245,9 @@ int g_cfg = -1;   // chosen once per process
 
 int k2_config() {
   if (g_cfg < 0) {
-    int c = 1;
+    int c = 2;
     if (const char* e = std::getenv("TRIMUL_K2_TILE")) c = std::atoi(e);
-    g_cfg = (c >= 0 && c <= 3) ? c : 1;
+    g_cfg = (c >= 0 && c <= 3) ? c : 2;
   }
   return g_cfg;
 }
@@ -266,9 +263,9 @@ void tiles_of(int N, int& tm, int& tn) {
 void k2_tiles(int N, int& tiles_m, int& tiles_n) {
   switch (k2_config()) {
     case 0: tiles_of<CfgSq32>(N, tiles_m, tiles_n); break;
-    case 2: tiles_of<CfgSq64>(N, tiles_m, tiles_n); break;
     case 3: tiles_of<CfgTall64>(N, tiles_m, tiles_n); break;
-    default: tiles_of<CfgRect64>(N, tiles_m, tiles_n); break;
+    case 1: tiles_of<CfgRect64>(N, tiles_m, tiles_n); break;
+    default: tiles_of<CfgSq64>(N, tiles_m, tiles_n); break;
   }
 }
 
@@ -281,9 +278,9 @@ void launch_cfg(const K2Args& a, hipStream_t stream) {
 hipError_t launch_k2(const K2Args& a, hipStream_t stream) {
   switch (k2_config()) {
     case 0: launch_cfg<CfgSq32>(a, stream); break;
-    case 2: launch_cfg<CfgSq64>(a, stream); break;
     case 3: launch_cfg<CfgTall64>(a, stream); break;
-    default: launch_cfg<CfgRect64>(a, stream); break;
+    case 1: launch_cfg<CfgRect64>(a, stream); break;
+    default: launch_cfg<CfgSq64>(a, stream); break;
   }
   return hipGetLastError();
 }

@@ -152,7 +152,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
 #pragma unroll
       for (int v = 0; v < NV; ++v) st16(sm.z + soff<C>(lp, sub + 8 * v), z[v]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- prefetch the next tile while this one is processed ----
     if (t + gridDim.x < p.ntiles) prefetch(t + gridDim.x);
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
 #pragma unroll
       for (int v = 0; v < NV; ++v) st16(sm.y + soff<C>(lp, sub + 8 * v), u[v]);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- output projection and gate: D[out channel][pair] ----
 #pragma unroll
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
         *reinterpret_cast<u32x2*>(sm.o + soff<C>(prow, 4 * nb + rg) + 8 * lhi) = packed;
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- coalesced pair-major stores of out ----
 #pragma unroll

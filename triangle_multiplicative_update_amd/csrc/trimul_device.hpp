@@ -42,6 +42,17 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ bf16x8 ld_frag(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// ------------------------------------------------------- block barrier ----
+// A workgroup barrier that orders LDS only: waits for this wave's LDS
+// operations, then meets the other waves. __syncthreads() would also drain
+// every outstanding global load and store (s_waitcnt vmcnt(0)), serializing
+// the memory traffic of a tile with the compute of the next. The "memory"
+// clobber keeps the compiler from moving LDS accesses across it; global
+// memory is never used to communicate between waves of a block.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ------------------------------------------------------- cross-lane sums ---
 
 template <int CTRL>
