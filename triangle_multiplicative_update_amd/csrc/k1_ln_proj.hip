@@ -16,13 +16,18 @@
 // channels' value and gate weight rows (2 x 32 x c_z bf16) in registers for
 // the whole kernel, so the weights are read once per block, not per tile.
 //
-// Software pipeline, one barrier per tile: the block stores tile t-1's staged
-// channel-major outputs with 16-byte coalesced writes, then -- while the
-// matrix cores multiply tile t (MFMA 32x32x16, M = pairs, N = channels, K =
-// c_z, value and gate accumulators side by side) and the VALU applies
-// sigmoid * value * mask -- runs LayerNorm of tile t+1 into the other z
-// buffer and issues the x loads of tile t+2. z, mask and output staging are
-// double-buffered in LDS.
+// Software pipeline. Each wave splits its multiply into two halves of 32
+// pairs and overlaps the matrix cores with the VALU across tile boundaries:
+// while the MFMAs of half 1 of tile t run, the wave applies sigmoid * value *
+// mask to half 0 of tile t; while the MFMAs of half 0 of tile t+1 run, it
+// finishes half 1 of tile t. Between the two, LayerNorm of tile t+1 goes into
+// the other z buffer and the x loads of tile t+2 are issued; after the one
+// barrier per tile, the block stores tile t-1's staged channel-major outputs
+// with 16-byte coalesced writes. z and the mask are double-buffered in LDS,
+// the output staging triple-buffered (double for c_z = 256, with a second
+// barrier), so no buffer is overwritten while another wave still reads it.
+
+#include <type_traits>
 
 #include "trimul_device.hpp"
 #include "trimul_kernels.hpp"
@@ -33,8 +38,9 @@ namespace {
 
 constexpr int K1_THREADS = 512;
 
-// bf16 1.0: the mask value read (at index 0) when the call has no mask
-__device__ const uint16_t kMaskOne[1] = {0x3F80};
+// bf16 1.0 and +0.0: the mask values read for pairs of a call without a mask
+// and for pairs past N
+__device__ const uint16_t kMaskConst[2] = {0x3F80, 0x0000};
 constexpr int K1_TP = 64;          // pairs per tile
 constexpr int K1_GROUP = 128;      // channels of a (and of b) per block
 
@@ -42,8 +48,9 @@ template <int CZ>
 struct K1Smem {
   static constexpr int ZP = CZ + 8;        // z row pitch (bf16 elements)
   static constexpr int OP = K1_TP + 8;     // staging row pitch
+  static constexpr int OB = CZ == 128 ? 3 : 2;   // output staging buffers
   uint16_t z[2][K1_TP * ZP];
-  uint16_t o[2][2 * K1_GROUP * OP];
+  uint16_t o[OB][2 * K1_GROUP * OP];
   float m[2][K1_TP];
 };
 
@@ -72,8 +79,18 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
     wv[ks] = ld_frag(p.p_in + size_t(wrow) * CZ + 16 * ks + 8 * lhi);
     wg[ks] = ld_frag(p.g_in + size_t(wrow) * CZ + 16 * ks + 8 * lhi);
   }
-  const float bias_v = p.p_in_b ? bf16_to_f32(p.p_in_b[wrow]) : 0.0f;
-  const float bias_g = p.g_in_b ? bf16_to_f32(p.g_in_b[wrow]) : 0.0f;
+  // the biases enter as the accumulator input of the first MFMA of a chain
+  // (every register of a lane's accumulator belongs to the lane's channel)
+  f32x16 bias_v, bias_g;
+  {
+    const float bv = p.p_in_b ? bf16_to_f32(p.p_in_b[wrow]) : 0.0f;
+    const float bg = p.g_in_b ? bf16_to_f32(p.g_in_b[wrow]) : 0.0f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      bias_v[r] = bv;
+      bias_g[r] = bg;
+    }
+  }
 
   // ---- LayerNorm lane mapping: pair `lp`, sub-lane `sub` ----
   const int lp = tid >> 3;
@@ -92,140 +109,166 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
   const size_t ch_stride = size_t(p.B) * N * p.n_pad;
   // no mask: every pair reads the constant 1.0 (index stride 0), so the mask
   // load needs no branch (a branch would force a wait on all memory traffic)
-  const uint16_t* mask = p.mask ? p.mask : kMaskOne;
+  const uint16_t* mask = p.mask ? p.mask : kMaskConst;
   const int mask_step = p.mask ? 1 : 0;
 
-  // x and mask of this lane's LayerNorm pair in tile t; pairs past N read a
-  // valid pair and are then zeroed (mask 0), so no branch is needed.
+  // x and mask of this lane's LayerNorm pair in tile t, as loaded; pairs past
+  // N read a valid pair's x (zeroed when LayerNorm consumes it) and the mask
+  // constant 0. No instruction uses the loaded values before LayerNorm, so
+  // nothing waits for the loads until then.
   u32x4 xr[NV];
-  float mr = 0.0f;
+  uint16_t mraw = 0;
+  bool xok = false;
   auto fetch = [&](int t) {
     const int row = t / nchunk;
     const int inner = (t - row * nchunk) * K1_TP + lp;
-    const bool ok = inner < N;
-    const int in_c = ok ? inner : N - 1;
+    xok = inner < N;
+    const int in_c = xok ? inner : N - 1;
     const int bb = row / N;
     const int fixed = row - bb * N;
     // outgoing: pair (b, fixed, inner); incoming: pair (b, inner, fixed)
     const int pi = p.incoming ? (bb * N + in_c) * N + fixed : row * N + in_c;
 #pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      const u32x4 x = ld16(p.x + size_t(pi) * CZ + 8 * sub + 64 * v);
-      xr[v] = ok ? x : u32x4{0, 0, 0, 0};
-    }
-    const float m = bf16_to_f32(mask[pi * mask_step]);
-    mr = ok ? m : 0.0f;
+    for (int v = 0; v < NV; ++v) xr[v] = ld16(p.x + size_t(pi) * CZ + 8 * sub + 64 * v);
+    mraw = ld_global_u16(xok ? mask + pi * mask_step : kMaskConst + 1);
   };
 
-  // LayerNorm_in of the fetched tile -> z (bf16) and mask in LDS buffer `buf`
-  auto ln_store = [&](int buf) {
-    u32x4 z[NV];
-    layer_norm_row<NV>(xr, lnw, lnb, p.eps, z);
+  // LayerNorm_in of the fetched tile -> z (bf16) and mask in LDS buffer `zb`
+  auto ln_store = [&](int zb) {
+    u32x4 xin[NV], z[NV];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) st16(&sm.z[buf][lp * S::ZP + 8 * sub + 64 * v], z[v]);
-    sm.m[buf][lp] = mr;       // the 8 lanes of a pair write the same value
+    for (int v = 0; v < NV; ++v) xin[v] = xok ? xr[v] : u32x4{0, 0, 0, 0};
+    layer_norm_row<NV>(xin, lnw, lnb, p.eps, z);
+#pragma unroll
+    for (int v = 0; v < NV; ++v) st16(&sm.z[zb][lp * S::ZP + 8 * sub + 64 * v], z[v]);
+    sm.m[zb][lp] = bf16_bits_late(mraw);   // the 8 lanes of a pair write the same value
   };
 
-  // projections of the tile in z buffer `buf`, gate * value * mask, bf16,
-  // staged channel-major in output buffer `buf`
-  auto mma_epi = [&](int buf) {
-    f32x16 acc_v[2], acc_g[2];
+  // One overlapped half step. With DO_MMA: the 2 * KS MFMAs of pair half
+  // `mb` of the tile in z buffer `zb` into (nv, ng). Interleaved with them:
+  // sigmoid(eg) * ev * mask for pair half `emb` of the tile whose mask is in
+  // buffer `ezb`, rounded to bf16 and staged channel-major in output buffer
+  // `ob`. The accumulator layout puts 4 consecutive pairs of one channel in
+  // each register group, i.e. 8 contiguous bytes of a staging row.
+  auto half = [&](auto do_mma, int zb, int mb, f32x16& nv, f32x16& ng, const f32x16& ev,
+                  const f32x16& eg, int ezb, int emb, int ob, auto&& each_rg) {
+    constexpr bool kMma = decltype(do_mma)::value;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int rg = 0; rg < 4; ++rg) {
+      each_rg(rg);
+      if constexpr (kMma) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc_v[mb][r] = bias_v;
-        acc_g[mb][r] = bias_g;
+        for (int kk = 0; kk < KS / 4; ++kk) {
+          const int ks = rg * (KS / 4) + kk;
+          const bf16x8 a = ld_frag(&sm.z[zb][(32 * mb + l32) * S::ZP + 16 * ks + 8 * lhi]);
+          nv = mfma32x32x16(a, wv[ks], ks == 0 ? bias_v : nv);
+          ng = mfma32x32x16(a, wg[ks], ks == 0 ? bias_g : ng);
+        }
       }
+      const int m0 = 32 * emb + 8 * rg + 4 * lhi;   // first of 4 consecutive pairs
+      const f32x4 mm = *reinterpret_cast<const f32x4*>(&sm.m[ezb][m0]);
+      float o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = 4 * rg + q;
+        o[q] = __builtin_fmaf(sigmoid_f(eg[r]) * ev[r], mm[q], 0.0f);   // +0.0 for m = 0
+      }
+      const u32x2 packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      *reinterpret_cast<u32x2*>(&sm.o[ob][(plane * K1_GROUP + chs + l32) * S::OP + m0]) = packed;
     }
+  };
+
+  // the MFMAs of a half step on their own (first tile of the block)
+  auto mma_only = [&](int zb, int mb, f32x16& nv, f32x16& ng) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a = ld_frag(&sm.z[buf][(32 * mb + l32) * S::ZP + 16 * ks + 8 * lhi]);
-        acc_v[mb] = mfma32x32x16(a, wv[ks], acc_v[mb]);
-        acc_g[mb] = mfma32x32x16(a, wg[ks], acc_g[mb]);
-      }
-    }
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        const int m0 = 32 * mb + 8 * rg + 4 * lhi;   // first of 4 consecutive pairs
-        const f32x4 mm = *reinterpret_cast<const f32x4*>(&sm.m[buf][m0]);
-        float o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int r = 4 * rg + q;
-          o[q] = sigmoid_f(acc_g[mb][r]) * acc_v[mb][r] * mm[q] + 0.0f;
-        }
-        const u32x2 packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        *reinterpret_cast<u32x2*>(&sm.o[buf][(plane * K1_GROUP + chs + l32) * S::OP + m0]) = packed;
-      }
+      const bf16x8 a = ld_frag(&sm.z[zb][(32 * mb + l32) * S::ZP + 16 * ks + 8 * lhi]);
+      nv = mfma32x32x16(a, wv[ks], ks == 0 ? bias_v : nv);
+      ng = mfma32x32x16(a, wg[ks], ks == 0 ? bias_g : ng);
     }
   };
 
-  // coalesced plane stores of tile t from output buffer `buf`: 256 rows
-  // (128 a + 128 b channels) x 64 pairs; n_pad is a multiple of 64, so every
-  // 16-byte chunk of the tile lies inside its row
-  auto store = [&](int t, int buf) {
+  // coalesced plane stores of tile t from output buffer `ob`: 256 rows
+  // (128 a + 128 b channels) x 64 pairs, one 16-byte chunk per thread and
+  // part `it` (0..3); n_pad is a multiple of 64, so every chunk of the tile
+  // lies inside its row
+  constexpr int kStoreParts = (2 * K1_GROUP * K1_TP / 8) / K1_THREADS;
+  auto store_part = [&](int t, int ob, int it) {
     const int row = t / nchunk;
     const int inner0 = (t - row * nchunk) * K1_TP;
-#pragma unroll
-    for (int it = 0; it < (2 * K1_GROUP * K1_TP / 8) / K1_THREADS; ++it) {
-      const int id = it * K1_THREADS + tid;
-      const int srow = id >> 3;              // staging row: plane * 128 + channel
-      const int c16 = id & 7;
-      const int pl = srow / K1_GROUP;
-      const int gch = group * K1_GROUP + (srow - pl * K1_GROUP);
-      uint16_t* dst = (pl ? p.plane_b : p.plane_a) + size_t(gch) * ch_stride + size_t(row) * p.n_pad +
-                      inner0 + 8 * c16;
-      st16(dst, ld16(&sm.o[buf][srow * S::OP + 8 * c16]));
-    }
+    const int id = it * K1_THREADS + tid;
+    const int srow = id >> 3;              // staging row: plane * 128 + channel
+    const int c16 = id & 7;
+    const int pl = srow / K1_GROUP;
+    const int gch = group * K1_GROUP + (srow - pl * K1_GROUP);
+    uint16_t* dst = (pl ? p.plane_b : p.plane_a) + size_t(gch) * ch_stride + size_t(row) * p.n_pad +
+                    inner0 + 8 * c16;
+    st16(dst, ld16(&sm.o[ob][srow * S::OP + 8 * c16]));
   };
+  auto store = [&](int t, int ob) {
+#pragma unroll
+    for (int it = 0; it < kStoreParts; ++it) store_part(t, ob, it);
+  };
+  auto no_op = [](int) {};
 
   int t = blockIdx.x;
   if (t >= ntiles) return;
-  // prologue: LayerNorm of the first tile, x of the second in flight
+  f32x16 v0, g0, v1, g1;   // accumulators of pair halves 0 and 1
+
+  // prologue: LayerNorm of the first tile, x of the second in flight, the
+  // MFMAs of the first tile's half 0
   fetch(t);
   ln_store(0);
   if (t + stride < ntiles) fetch(t + stride);
   lds_barrier();
+  mma_only(0, 0, v0, g0);
 
-  // first tile (nothing staged for storing yet)
-  int k = 0;
-  {
-    mma_epi(0);
-    if (t + stride < ntiles) {
-      ln_store(1);
-      if (t + 2 * stride < ntiles) fetch(t + 2 * stride);
+  // One tile t with z buffer zb, output buffer ob; `prev` names the output
+  // buffer of the block's previous tile, still to be stored. kStore: 0 = no
+  // previous tile, 1 = one store part per register group of the overlapped
+  // half step (the stores trickle out between the MFMAs instead of stalling
+  // every wave at once), 2 = whole store if prev >= 0 (the last tiles).
+  int zb = 0, ob = 0, prev = -1;
+  auto tile = [&](auto store_mode, auto has_next, auto has_next2) {
+    constexpr int kStore = decltype(store_mode)::value;
+    constexpr bool kNext = decltype(has_next)::value;
+    constexpr bool kNext2 = decltype(has_next2)::value;
+    // half 1's MFMAs || half 0's gate epilogue
+    half(std::true_type{}, zb, 1, v1, g1, v0, g0, zb, 0, ob, no_op);
+    if constexpr (kNext) ln_store(zb ^ 1);
+    if constexpr (kNext2) fetch(t + 2 * stride);
+    lds_barrier();
+    if constexpr (kStore == 2) {
+      if (prev >= 0) store(t - stride, prev);
     }
-    lds_barrier();
+    if constexpr (S::OB == 2) {
+      if constexpr (kStore == 1) store(t - stride, prev);
+      lds_barrier();
+    }
+    // next tile's half-0 MFMAs || half 1's gate epilogue (|| the stores)
+    const int tp = t - stride, pb = prev;
+    auto st = [&](int rg) {
+      if constexpr (kStore == 1 && S::OB != 2) {
+        if (rg < kStoreParts) store_part(tp, pb, rg);
+      }
+    };
+    if constexpr (kNext) half(std::true_type{}, zb ^ 1, 0, v0, g0, v1, g1, zb, 1, ob, st);
+    else half(std::false_type{}, 0, 0, v0, g0, v1, g1, zb, 1, ob, st);
+    prev = ob;
+    ob = (ob + 1 == S::OB) ? 0 : ob + 1;
+    zb ^= 1;
     t += stride;
-    k = 1;
-  }
-  // Steady state: every part unconditional, one basic block per tile. The
-  // stores of tile t-1 go first: with stores and loads both in flight the
-  // memory counter only supports waiting for all of them, and the first use
-  // of the prefetched x (LayerNorm of tile t+1) comes after the whole
-  // multiply phase, by which time the stores have long completed.
-  for (; t + 2 * stride < ntiles; t += stride, ++k) {
-    const int cur = k & 1;
-    store(t - stride, cur ^ 1);
-    mma_epi(cur);
-    ln_store(cur ^ 1);
-    fetch(t + 2 * stride);
-    lds_barrier();
-  }
-  // the last (at most two) tiles
-  for (; t < ntiles; t += stride, ++k) {
-    const int cur = k & 1;
-    store(t - stride, cur ^ 1);
-    mma_epi(cur);
-    if (t + stride < ntiles) ln_store(cur ^ 1);
-    lds_barrier();
-  }
-  store(t - stride, (k - 1) & 1);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  // steady state: every part unconditional
+  if (t + 2 * stride < ntiles) tile(I0{}, std::true_type{}, std::true_type{});
+  while (t + 2 * stride < ntiles) tile(I1{}, std::true_type{}, std::true_type{});
+  if (t + stride < ntiles) tile(I2{}, std::true_type{}, std::false_type{});
+  tile(I2{}, std::false_type{}, std::false_type{});
+  lds_barrier();
+  store(t - stride, prev);
 }
 
 }  // namespace

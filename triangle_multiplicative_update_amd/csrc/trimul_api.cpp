@@ -16,7 +16,7 @@
 #include <mutex>
 #include <string>
 
-#include "../../include/trimul.h"
+#include "trimul.h"
 #include "trimul_kernels.hpp"
 
 namespace {

@@ -42,6 +42,24 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ bf16x8 ld_frag(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+// One bf16 from global memory. The address-space cast makes it a global load:
+// a flat load also counts against the LDS wait counter, so every later LDS
+// wait or barrier would wait for it too.
+__device__ __forceinline__ uint16_t ld_global_u16(const uint16_t* p) {
+  return *(const __attribute__((address_space(1))) uint16_t*)(p);
+}
+
+// bf16 bits -> float, as an instruction the compiler cannot fold back to the
+// load that produced them (the shift discards whatever the register's upper
+// half holds). A prefetched value converted by plain code is turned into a
+// conversion right after its load, and the wait for that load then lands in
+// the middle of the work meant to hide it.
+__device__ __forceinline__ float bf16_bits_late(uint16_t h) {
+  float r;
+  asm volatile("v_lshlrev_b32 %0, 16, %1" : "=v"(r) : "v"(h));
+  return r;
+}
+
 // ------------------------------------------------------- block barrier ----
 // A workgroup barrier that orders LDS only: waits for this wave's LDS
 // operations, then meets the other waves. __syncthreads() would also drain
