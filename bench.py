@@ -14,7 +14,6 @@ and the CPU oracle's time on this host (a baseline, not a target).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -23,41 +22,34 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from triangle_multiplicative_update_amd.profiling import KERNEL_NAMES, kernel_sha  # noqa: E402
+
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_FILES = {1: "k1_ln_proj.hip", 2: "k2_contract.hip", 3: "k3_epilogue.hip"}
-KERNEL_NAMES = {1: "k1_ln_proj", 2: "k2_contract", 3: "k3_epilogue"}
 MFMA_BALANCE = 2516.6e12 / 8000e9       # flop per byte where the two roofs meet
 
 
 def parse():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None, help="workload name (default: the N=768 one)")
     ap.add_argument("--direction", default="outgoing", choices=["outgoing", "incoming"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="time the oracle on this many output rows only (0 = the whole call)")
+    ap.add_argument("--profile-dir", default=None,
+                    help="where the HBM traffic records are read (default: profiles/)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run --steps plain device copies of this many MiB (for scaling "
                          "the HBM byte counters) and exit")
     return ap.parse_args()
 
 
-def kernel_sha(stage: int) -> str:
-    csrc = os.path.join(ROOT, "triangle_multiplicative_update_amd", "csrc")
-    h = hashlib.sha256()
-    for f in (KERNEL_FILES[stage], "trimul_device.hpp", "trimul_kernels.hpp"):
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
-def measured_traffic(stage: int, workload: str, direction: str):
+def measured_traffic(stage: int, workload: str, direction: str, profile_dir: str = PROFILE_DIR):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel source; else None."""
-    path = os.path.join(PROFILE_DIR, f"traffic_{KERNEL_NAMES[stage]}_{workload}_{direction}.json")
+    path = os.path.join(profile_dir, f"traffic_{KERNEL_NAMES[stage]}_{workload}_{direction}.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -183,7 +175,7 @@ def main():
         roof = {"bound": "hbm", "achieved": sb[dom] / ts / 1e9, "peak": perf_model.PEAK_HBM_GBS,
                 "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(dom + 1, name, direction)
+    roof["traffic"] = measured_traffic(dom + 1, name, direction, args.profile_dir or PROFILE_DIR)
     roof["kernel"] = KERNEL_NAMES[dom + 1]
     roof["kernel_us"] = per_stage_ms[dom] * 1e3
     roof["algorithmic_bytes"] = sb[dom]

@@ -1,0 +1,191 @@
+"""Turn rocprofv3 output into the measurement records kept under profiles/.
+
+Two kinds of record:
+
+* HBM traffic per launch of each stage kernel, from two counter passes
+  (``--pmc FETCH_SIZE`` and ``--pmc WRITE_SIZE``, each its own run) of
+  ``bench.py``, scaled by what the same counters read for plain device copies
+  of a known size (``bench.py --copy-calibration-mib``). One JSON file per
+  kernel (``traffic_<kernel>_<workload>_<direction>.json``) carries the bytes
+  and a hash of the kernel sources, so ``bench.py`` only reports them while
+  the kernel is unchanged, plus a Markdown summary.
+* A kernel-trace summary (``--kernel-trace --stats``) as Markdown.
+
+Usage (each counter pass is a separate rocprofv3 run; see the written
+summaries for the exact commands)::
+
+    python -m triangle_multiplicative_update_amd.profiling traffic \\
+        --fetch DIR --write DIR --cal-fetch DIR --cal-write DIR --cal-mib 512 \\
+        --workload n768_c128_pad700 --direction outgoing --out profiles
+    python -m triangle_multiplicative_update_amd.profiling trace \\
+        --stats DIR --workload n768_c128_pad700 --direction outgoing --out profiles
+"""
+
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+KERNEL_FILES = {1: "k1_ln_proj.hip", 2: "k2_contract.hip", 3: "k3_epilogue.hip"}
+KERNEL_NAMES = {1: "k1_ln_proj", 2: "k2_contract", 3: "k3_epilogue"}
+SHARED_FILES = ("trimul_device.hpp", "trimul_kernels.hpp")
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def kernel_sha(stage: int) -> str:
+    """Hash of the sources a stage kernel is built from."""
+    h = hashlib.sha256()
+    for f in (KERNEL_FILES[stage], *SHARED_FILES):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stage_of(kernel_name: str):
+    for s, n in KERNEL_NAMES.items():
+        if n + "<" in kernel_name:
+            return s
+    return None
+
+
+def _csv_rows(directory: str, suffix: str):
+    files = glob.glob(os.path.join(directory, "**", f"*{suffix}"), recursive=True)
+    if not files:
+        raise FileNotFoundError(f"no *{suffix} under {directory}")
+    for f in files:
+        with open(f, newline="") as fh:
+            yield from csv.DictReader(fh)
+
+
+def counter_per_dispatch(directory: str, counter: str):
+    """{kernel name: [counter value of each dispatch]} from a --pmc run."""
+    out: dict[str, list[float]] = {}
+    for row in _csv_rows(directory, "counter_collection.csv"):
+        if row.get("Counter_Name") != counter:
+            continue
+        out.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    return out
+
+
+def _median_for(values: dict, pred):
+    vs = [v for k, lst in values.items() if pred(k) for v in lst]
+    if not vs:
+        raise KeyError("no matching dispatch")
+    return statistics.median(vs)
+
+
+def traffic(args) -> None:
+    from . import perf_model
+    import synthetic_inputs as si
+
+    wl = si.WORKLOADS[args.workload]
+    fetch = counter_per_dispatch(args.fetch, "FETCH_SIZE")
+    write = counter_per_dispatch(args.write, "WRITE_SIZE")
+    cal_bytes = args.cal_mib * 2 ** 20
+    # a copy reads and writes cal_bytes once each; the counters are in KiB
+    cal_f = _median_for(counter_per_dispatch(args.cal_fetch, "FETCH_SIZE"), lambda k: COPY_KERNEL in k)
+    cal_w = _median_for(counter_per_dispatch(args.cal_write, "WRITE_SIZE"), lambda k: COPY_KERNEL in k)
+    f_scale = cal_bytes / (cal_f * 1024.0)
+    w_scale = cal_bytes / (cal_w * 1024.0)
+    sb = perf_model.stage_bytes(wl.B, wl.N, wl.c_z, wl.c, mask=wl.mask != "none")
+    bench_cmd = f"python3 bench.py --steps 3 --warmup 1 --no-cpu-baseline --workload {args.workload} --direction {args.direction}"
+    cmds = [
+        f"rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir> -o run -- {bench_cmd}",
+        f"rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir> -o run -- {bench_cmd}",
+        f"rocprofv3 --pmc FETCH_SIZE (then WRITE_SIZE) --output-format csv -d <dir> -o run -- "
+        f"python3 bench.py --steps 3 --copy-calibration-mib {args.cal_mib}",
+    ]
+    rows = []
+    for s in (1, 2, 3):
+        name = KERNEL_NAMES[s]
+        fk = _median_for(fetch, lambda k: stage_of(k) == s)
+        wk = _median_for(write, lambda k: stage_of(k) == s)
+        rec = {
+            "kernel": name,
+            "workload": args.workload,
+            "direction": args.direction,
+            "kernel_sha": kernel_sha(s),
+            "hbm_bytes_per_launch": fk * 1024 * f_scale + wk * 1024 * w_scale,
+            "fetch_bytes": fk * 1024 * f_scale,
+            "write_bytes": wk * 1024 * w_scale,
+            "algorithmic_bytes": sb[s - 1],
+            "fetch_kib_raw": fk,
+            "write_kib_raw": wk,
+            "fetch_scale": f_scale,
+            "write_scale": w_scale,
+            "commands": cmds,
+        }
+        with open(os.path.join(args.out, f"traffic_{name}_{args.workload}_{args.direction}.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+        rows.append(rec)
+    md = [f"# HBM traffic per launch: {args.workload}, {args.direction}", "",
+          "Commands (each its own rocprofv3 run, from /tmp, repository at $R):", "", "```"]
+    md += [c.replace("python3 bench.py", "python3 $R/bench.py") for c in cmds]
+    md += ["```", "",
+           f"Calibration: a {args.cal_mib} MiB device copy (`{COPY_KERNEL}`, {args.cal_mib} MiB read + "
+           f"{args.cal_mib} MiB written) reads FETCH_SIZE = {cal_f:.0f} KiB and WRITE_SIZE = {cal_w:.0f} KiB, "
+           f"so FETCH_SIZE is scaled by {f_scale:.4f} and WRITE_SIZE by {w_scale:.4f} to bytes.", "",
+           "| kernel | FETCH_SIZE (KiB, raw) | WRITE_SIZE (KiB, raw) | HBM read (MB) | HBM write (MB) | "
+           "total (MB) | algorithmic (MB) | ratio |",
+           "|---|---|---|---|---|---|---|---|"]
+    for r in rows:
+        md.append(f"| {r['kernel']} | {r['fetch_kib_raw']:.0f} | {r['write_kib_raw']:.0f} | "
+                  f"{r['fetch_bytes'] / 1e6:.1f} | {r['write_bytes'] / 1e6:.1f} | "
+                  f"{r['hbm_bytes_per_launch'] / 1e6:.1f} | {r['algorithmic_bytes'] / 1e6:.1f} | "
+                  f"{r['hbm_bytes_per_launch'] / r['algorithmic_bytes']:.3f} |")
+    md += ["", f"The per-kernel records `traffic_<kernel>_{args.workload}_{args.direction}.json` carry these "
+           "numbers with a hash of the kernel sources they were taken on; `bench.py` reports them as "
+           "`roofline.traffic` only while the hash matches.", ""]
+    with open(os.path.join(args.out, f"hbm_traffic_{args.workload}_{args.direction}.md"), "w") as fh:
+        fh.write("\n".join(md))
+
+
+def trace(args) -> None:
+    rows = list(_csv_rows(args.stats, "kernel_stats.csv"))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    md = [f"# Kernel trace: {args.workload}, {args.direction}", "",
+          "Command (run from /tmp on the MI355X box, repository at $R):", "", "```",
+          f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- python3 $R/bench.py "
+          f"{args.bench_args}", "```", "", "`run_kernel_stats.csv`:", "",
+          "| kernel | calls | average (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        md.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                  f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                  f"{100 * float(r['TotalDurationNs']) / total:.1f} % |")
+    if args.bench_json:
+        with open(args.bench_json) as fh:
+            line = [l for l in fh if l.startswith("{")][-1]
+        rec = json.loads(line)
+        md += ["", "The same process's own HIP-event timing of the timed steps (`per_stage_us` of its JSON line):",
+               "", "```", json.dumps(rec.get("per_stage_us")), "```"]
+    md.append("")
+    with open(os.path.join(args.out, f"kernel_trace_{args.workload}_{args.direction}.md"), "w") as fh:
+        fh.write("\n".join(md))
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    for a in ("--fetch", "--write", "--cal-fetch", "--cal-write", "--workload", "--direction", "--out"):
+        t.add_argument(a, required=True)
+    t.add_argument("--cal-mib", type=int, required=True)
+    k = sub.add_parser("trace")
+    for a in ("--stats", "--workload", "--direction", "--out"):
+        k.add_argument(a, required=True)
+    k.add_argument("--bench-args", default="")
+    k.add_argument("--bench-json", default=None, help="file holding the profiled run's JSON line")
+    args = ap.parse_args()
+    os.makedirs(args.out, exist_ok=True)
+    (traffic if args.cmd == "traffic" else trace)(args)
+
+
+if __name__ == "__main__":
+    main()
