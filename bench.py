@@ -154,6 +154,19 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
 
+        # the same call as one captured graph launch per step (host overhead of
+        # three eager launches removed), timed the same way
+        graph = prep.graph()
+        for _ in range(args.warmup):
+            graph.launch()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for _ in range(K):
+            graph.launch()
+        torch.cuda.synchronize()
+        graph_wall = time.perf_counter() - tg
+        graph.close()
+
     per_stage_ms = [float(np.mean([ev[k][s].elapsed_time(ev[k][s + 1]) for k in range(K)]))
                     for s in range(3)]
     span_ms = ev[0][0].elapsed_time(ev[K - 1][3]) / K      # device span per step
@@ -202,6 +215,7 @@ def main():
         "hbm_gbs_model": T / t / 1e9,
         "per_stage_us": {KERNEL_NAMES[s + 1]: per_stage_ms[s] * 1e3 for s in range(3)},
         "device_ms_per_step": span_ms,
+        "graph_ms_per_step": graph_wall * 1e3 / K,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -139,6 +139,43 @@ int trimul_forward_stage(int stage,
                          int B, int N, int c_z, int c, int direction, float eps,
                          void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Captured forward (same page, "Prepared class API": make_cuda_graph,
+ * "one graph launch per call for these buffers"; the small-N calls are host
+ * bound when launched eagerly). ----
+ *
+ * trimul_graph_create validates its arguments as trimul_forward does
+ * (including the device check, on the current HIP device), then captures the
+ * three stage launches for exactly these buffers into a HIP graph and
+ * instantiates it. It allocates (a capture stream, the graph) and
+ * synchronizes nothing on any caller stream; nothing runs until a launch. On
+ * success *graph receives an opaque handle; on failure *graph is set to NULL.
+ *
+ * trimul_graph_launch enqueues one forward pass on `stream` (a stream of the
+ * device the graph was created on; NULL = the null stream). The graph reads
+ * the buffers' contents at launch time, so callers may rewrite x, the mask
+ * and the parameters between launches; the buffers must stay allocated and
+ * keep their sizes while the handle lives. Launches of one handle on
+ * different streams must not overlap (they share the workspace).
+ *
+ * trimul_graph_destroy releases the handle (NULL is accepted). Work already
+ * launched completes normally. */
+typedef struct trimul_graph_s* trimul_graph_t;
+
+int trimul_graph_create(const void* x, const void* mask,
+                        const void* norm_in_w, const void* norm_in_b,
+                        const void* p_in_w, const void* p_in_b,
+                        const void* g_in_w, const void* g_in_b,
+                        const void* norm_out_w, const void* norm_out_b,
+                        const void* p_out_w, const void* p_out_b,
+                        const void* g_out_w, const void* g_out_b,
+                        int B, int N, int c_z, int c, int direction, float eps,
+                        void* out, void* workspace, size_t workspace_bytes,
+                        trimul_graph_t* graph);
+
+int trimul_graph_launch(trimul_graph_t graph, void* stream);
+
+int trimul_graph_destroy(trimul_graph_t graph);
+
 #ifdef __cplusplus
 }
 #endif

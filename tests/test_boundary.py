@@ -171,3 +171,42 @@ def test_python_declines_without_gpu():
     with torch.no_grad():
         with pytest.raises(ValueError, match="GPU"):
             api.triangle_multiplicative_update(xg, "outgoing", None, *params)
+
+
+def test_graph_handles_without_device():
+    # argument rules are checked before any HIP call; the handle is cleared
+    h = ctypes.c_void_p(1234)
+    a = good_args(x=None)
+    assert lib.trimul_graph_create(*[a[k] for k in ORDER], ctypes.byref(h)) == INVALID
+    assert h.value is None
+    assert "x is required" in _native.last_error()
+    a = good_args()
+    assert lib.trimul_graph_create(*[a[k] for k in ORDER], None) == INVALID
+    assert "NULL" in _native.last_error()
+    assert lib.trimul_graph_launch(None, None) == INVALID
+    assert lib.trimul_graph_destroy(None) == OK
+    if not torch.cuda.is_available():
+        h2 = ctypes.c_void_p(1234)
+        assert lib.trimul_graph_create(*[a[k] for k in ORDER], ctypes.byref(h2)) == DEVICE
+        assert h2.value is None
+
+
+def test_plan_declines_without_gpu():
+    with pytest.raises(ValueError, match="direction"):
+        api.TriangleMultiplicativeUpdateFwd((1, 8, 8, 128), "diagonal", 128, True, True, True)
+    with pytest.raises(ValueError, match="square"):
+        api.TriangleMultiplicativeUpdateFwd((1, 8, 9, 128), "outgoing", 128, True, True, True)
+    plan = api.TriangleMultiplicativeUpdateFwd((2, 77, 77, 256), "incoming", 256, False, False, True,
+                                               device="cpu")
+    assert plan.get_workspace_size() == workspace_bytes(2, 77, 256, "incoming")
+    with pytest.raises(ValueError, match="GPU"):
+        plan.check_support()
+    w = torch.zeros(128, dtype=torch.bfloat16)
+    m = torch.zeros(256, 128, dtype=torch.bfloat16)
+    o = torch.zeros(128, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        api.prepare_weights(w, w, m, None, m, None, w, w, o, None, o, None)
+    with pytest.raises(ValueError, match="required"):
+        api.prepare_weights(w, w, None, None, m, None, w, w, o, None, o, None)
+    with pytest.raises(NotImplementedError, match="precision"):
+        api.prepare_weights(w, w, m, None, m, None, w, w, o, None, o, None, precision="tf32")

@@ -34,6 +34,10 @@ SIGNATURES = {
     "trimul_validate": (_i, _TENSOR_ARGS + [_i, _i, _i, _i, _i, _f, _vp, _vp, _sz]),
     "trimul_forward": (_i, _TENSOR_ARGS + [_i, _i, _i, _i, _i, _f, _vp, _vp, _sz, _vp]),
     "trimul_forward_stage": (_i, [_i] + _TENSOR_ARGS + [_i, _i, _i, _i, _i, _f, _vp, _vp, _sz, _vp]),
+    "trimul_graph_create": (_i, _TENSOR_ARGS + [_i, _i, _i, _i, _i, _f, _vp, _vp, _sz,
+                                                ctypes.POINTER(_vp)]),
+    "trimul_graph_launch": (_i, [_vp, _vp]),
+    "trimul_graph_destroy": (_i, [_vp]),
 }
 
 

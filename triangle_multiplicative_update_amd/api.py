@@ -9,6 +9,7 @@ and the stream; every step of the computation runs in the HIP kernels.
 
 from __future__ import annotations
 
+import ctypes
 from typing import Optional
 
 import torch
@@ -226,3 +227,204 @@ class Prepared:
 
     def stage(self, s: int) -> None:
         raise_for_status(lib.trimul_forward_stage(s, *self.args), f"stage {s}")
+
+    def graph(self) -> "TrimulGraph":
+        """The same call captured once (one graph launch per call)."""
+        h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            raise_for_status(lib.trimul_graph_create(*self.args[:-1], ctypes.byref(h)), "graph")
+        return TrimulGraph(h.value, self.device, self._keep)
+
+
+# ---------------------------------------------------------------------------
+# Prepared class API (page "Triangle Multiplicative Update (SM100 / SM103 /
+# SM107)", section "Prepared class API"): parameters prepared once, a plan
+# declared for one geometry, execute() with no allocation and no sync, and a
+# captured graph per buffer set for the host-bound small-N calls.
+# ---------------------------------------------------------------------------
+
+class PreparedWeights:
+    """The twelve parameters, checked once: bf16, contiguous, one device, the
+    declared shapes. A bias given on one side only (in: p_in / g_in, out:
+    p_out / g_out) is paired with zeros here, never per call."""
+
+    def __init__(self, tensors: dict, c_z: int, c: int, device):
+        self.tensors = tensors
+        self.c_z, self.c, self.device = c_z, c, device
+        self.has_in_bias = tensors["p_in_bias"] is not None
+        self.has_out_bias = tensors["p_out_bias"] is not None
+
+    def ptrs(self):
+        return [_ptr(self.tensors[n]) for n in _PARAM_ORDER]
+
+
+def prepare_weights(norm_in_weight, norm_in_bias, p_in_weight, p_in_bias, g_in_weight, g_in_bias,
+                    norm_out_weight, norm_out_bias, p_out_weight, p_out_bias, g_out_weight,
+                    g_out_bias, precision=None) -> PreparedWeights:
+    if precision in _DECLINED_PRECISION or precision not in _SERVED_PRECISION:
+        raise NotImplementedError(f"precision={precision!r} is not served")
+    params = dict(zip(_PARAM_ORDER, (norm_in_weight, norm_in_bias, p_in_weight, p_in_bias,
+                                      g_in_weight, g_in_bias, norm_out_weight, norm_out_bias,
+                                      p_out_weight, p_out_bias, g_out_weight, g_out_bias)))
+    for n in _REQUIRED:
+        if params[n] is None:
+            raise ValueError(f"{n} is required")
+    device = params["p_in_weight"].device
+    if device.type != "cuda":
+        raise ValueError(f"parameters must be on a GPU device, got {device}")
+    for n in _PARAM_ORDER:
+        params[n] = _prep_param(n, params[n], precision, device)
+    two_c, c_z = params["p_in_weight"].shape
+    c = two_c // 2
+    shapes = {"norm_in_weight": (c_z,), "norm_in_bias": (c_z,), "p_in_weight": (2 * c, c_z),
+              "p_in_bias": (2 * c,), "g_in_weight": (2 * c, c_z), "g_in_bias": (2 * c,),
+              "norm_out_weight": (c,), "norm_out_bias": (c,), "p_out_weight": (c_z, c),
+              "p_out_bias": (c_z,), "g_out_weight": (c_z, c_z), "g_out_bias": (c_z,)}
+    for n, shp in shapes.items():
+        t = params[n]
+        if t is not None and tuple(t.shape) != shp:
+            raise ValueError(f"{n} must have shape {shp}, got {tuple(t.shape)}")
+    for a, b in (("p_in_bias", "g_in_bias"), ("p_out_bias", "g_out_bias")):
+        if (params[a] is None) != (params[b] is None):
+            given = a if params[a] is not None else b
+            other = b if given == a else a
+            params[other] = torch.zeros_like(params[given])
+    return PreparedWeights(params, c_z, c, device)
+
+
+class TrimulGraph:
+    """One forward pass captured for a fixed buffer set (a HIP graph owned by
+    the C library). ``launch()`` enqueues it; the buffers' contents are read
+    at launch time. Keep the buffers alive while the graph lives."""
+
+    def __init__(self, handle: int, device, keep):
+        self._h = handle
+        self.device = device
+        self._keep = keep
+
+    def launch(self, stream=None) -> None:
+        if self._h is None:
+            raise RuntimeError("graph is closed")
+        if stream is None:
+            s = torch.cuda.current_stream(self.device).cuda_stream
+        elif isinstance(stream, torch.cuda.Stream):
+            s = stream.cuda_stream
+        else:
+            s = int(stream)
+        with torch.cuda.device(self.device):
+            raise_for_status(lib.trimul_graph_launch(self._h, s), "graph launch")
+
+    replay = launch
+
+    def close(self) -> None:
+        if self._h is not None:
+            h, self._h = self._h, None
+            raise_for_status(lib.trimul_graph_destroy(h), "graph destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            if self._h is not None:
+                lib.trimul_graph_destroy(self._h)
+                self._h = None
+        except Exception:
+            pass
+
+
+class TriangleMultiplicativeUpdateFwd:
+    """A plan for one geometry: ``x`` (a tensor or its shape [B, N, N, c_z] /
+    [N, N, c_z]), the direction, c_hidden, and whether calls carry a mask and
+    the in/out projection biases. The flags are part of the declaration:
+    ``execute`` raises if its arguments do not match them."""
+
+    def __init__(self, x, direction, c_hidden, has_mask, has_in_bias, has_out_bias, eps=1e-5,
+                 device=None):
+        self.code = _direction_code(direction)
+        self.direction = direction
+        if isinstance(x, torch.Tensor):
+            shape, dev = tuple(x.shape), x.device
+        else:
+            shape, dev = tuple(x), torch.device(device) if device is not None else None
+        if len(shape) not in (3, 4):
+            raise ValueError(f"x must be [B, N, N, c_z] or [N, N, c_z], got shape {shape}")
+        self.batchless = len(shape) == 3
+        B, N, N2, c_z = (1, *shape) if self.batchless else shape
+        if N != N2:
+            raise ValueError(f"x must be square in its pair axes, got {shape}")
+        self.B, self.N, self.c_z, self.c = B, N, c_z, int(c_hidden)
+        self.shape = shape
+        self.device = dev if dev is not None else torch.device("cuda", torch.cuda.current_device())
+        self.has_mask, self.has_in_bias, self.has_out_bias = bool(has_mask), bool(has_in_bias), bool(has_out_bias)
+        self.eps = float(eps)
+
+    def check_support(self) -> None:
+        idx = self.device.index if self.device.type == "cuda" else None
+        if self.device.type != "cuda":
+            raise ValueError(f"plans run on a GPU device, got {self.device}")
+        check_support(self.B, self.N, self.c_z, self.c, self.direction,
+                      idx if idx is not None else torch.cuda.current_device())
+
+    def compile(self):
+        """The kernels are built ahead of time for gfx950: this only runs the
+        support checks (and loads the library)."""
+        self.check_support()
+        return self
+
+    def get_workspace_size(self) -> int:
+        return workspace_bytes(self.B, self.N, self.c, self.direction)
+
+    def _args(self, x, mask, weights, out, workspace):
+        if not isinstance(weights, PreparedWeights):
+            raise ValueError("weights must come from prepare_weights()")
+        if (mask is not None) != self.has_mask:
+            raise ValueError(f"plan declared has_mask={self.has_mask} but mask is "
+                             f"{'given' if mask is not None else 'None'}")
+        if weights.has_in_bias != self.has_in_bias or weights.has_out_bias != self.has_out_bias:
+            raise ValueError(f"plan declared has_in_bias={self.has_in_bias}, "
+                             f"has_out_bias={self.has_out_bias}; the weights have "
+                             f"{weights.has_in_bias}, {weights.has_out_bias}")
+        if weights.c != self.c or weights.c_z != self.c_z:
+            raise ValueError(f"weights are for c_z={weights.c_z}, c={weights.c}; the plan for "
+                             f"c_z={self.c_z}, c={self.c}")
+        for n, t in (("x", x), ("out", out)):
+            if not isinstance(t, torch.Tensor) or tuple(t.shape) not in (self.shape, (self.B, self.N, self.N, self.c_z)):
+                raise ValueError(f"{n} must have the declared shape {self.shape}")
+            if t.dtype != torch.bfloat16 or not t.is_contiguous() or t.device != self.device:
+                raise ValueError(f"{n} must be a contiguous bf16 tensor on {self.device}")
+        if mask is not None:
+            if mask.dtype != torch.bfloat16 or not mask.is_contiguous() or mask.device != self.device:
+                raise ValueError(f"mask must be a contiguous bf16 tensor on {self.device}")
+            if mask.numel() != self.B * self.N * self.N:
+                raise ValueError(f"mask must be [B, N, N] = {(self.B, self.N, self.N)}")
+        if workspace.device != self.device:
+            raise ValueError(f"workspace must be on {self.device}")
+        return ([_ptr(x), _ptr(mask)] + weights.ptrs() +
+                [self.B, self.N, self.c_z, self.c, self.code, self.eps, out.data_ptr(),
+                 workspace.data_ptr(), workspace.numel() * workspace.element_size()])
+
+    def execute(self, x, mask, weights, out, workspace, current_stream=None) -> None:
+        """Validates and enqueues the three stages; no allocation, no sync."""
+        args = self._args(x, mask, weights, out, workspace)
+        if current_stream is None:
+            s = torch.cuda.current_stream(self.device).cuda_stream
+        elif isinstance(current_stream, torch.cuda.Stream):
+            s = current_stream.cuda_stream
+        else:
+            s = int(current_stream)
+        with torch.cuda.device(self.device):
+            raise_for_status(lib.trimul_forward(*args, s), "execute")
+
+    def make_graph(self, x, mask, weights, out, workspace) -> TrimulGraph:
+        """Capture one forward pass for these buffers (one launch per call)."""
+        args = self._args(x, mask, weights, out, workspace)
+        h = ctypes.c_void_p()
+        with torch.cuda.device(self.device):
+            raise_for_status(lib.trimul_graph_create(*args, ctypes.byref(h)), "make_graph")
+        return TrimulGraph(h.value, self.device, (x, mask, weights, out, workspace))
+
+    make_cuda_graph = make_graph

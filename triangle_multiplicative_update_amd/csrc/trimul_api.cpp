@@ -275,6 +275,11 @@ int run(int first_stage, int last_stage, const void* x, const void* mask, const 
 
 }  // namespace
 
+struct trimul_graph_s {
+  hipGraphExec_t exec;
+  int device;
+};
+
 extern "C" {
 
 const char* trimul_version(void) { return "trimul-gfx950 0.1.0"; }
@@ -333,6 +338,74 @@ int trimul_forward_stage(int stage, const void* x, const void* mask, const void*
   return run(stage, stage, x, mask, norm_in_w, norm_in_b, p_in_w, p_in_b, g_in_w, g_in_b,
              norm_out_w, norm_out_b, p_out_w, p_out_b, g_out_w, g_out_b, B, N, c_z, c, direction,
              eps, out, workspace, workspace_bytes, stream);
+}
+
+int trimul_graph_create(const void* x, const void* mask, const void* norm_in_w,
+                        const void* norm_in_b, const void* p_in_w, const void* p_in_b,
+                        const void* g_in_w, const void* g_in_b, const void* norm_out_w,
+                        const void* norm_out_b, const void* p_out_w, const void* p_out_b,
+                        const void* g_out_w, const void* g_out_b, int B, int N, int c_z, int c,
+                        int direction, float eps, void* out, void* workspace,
+                        size_t workspace_bytes, trimul_graph_t* graph) {
+  if (!graph) return fail(TRIMUL_E_INVALID, "graph (the handle's destination) is NULL");
+  *graph = nullptr;
+  int st = check_args(x, mask, norm_in_w, norm_in_b, p_in_w, p_in_b, g_in_w, g_in_b, norm_out_w,
+                      norm_out_b, p_out_w, p_out_b, g_out_w, g_out_b, B, N, c_z, c, direction, eps,
+                      out, workspace, workspace_bytes);
+  if (st != TRIMUL_OK) return st;
+  // device properties are read (and cached) before the capture starts
+  DeviceInfo info;
+  st = current_device_check(info);
+  if (st != TRIMUL_OK) return st;
+  int dev = -1;
+  hipGetDevice(&dev);
+
+  hipStream_t cs = nullptr;
+  hipError_t e = hipStreamCreateWithFlags(&cs, hipStreamNonBlocking);
+  if (e != hipSuccess) return fail(TRIMUL_E_DEVICE, "hipStreamCreateWithFlags: %s", hipGetErrorString(e));
+  e = hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal);
+  if (e != hipSuccess) {
+    hipStreamDestroy(cs);
+    return fail(TRIMUL_E_DEVICE, "hipStreamBeginCapture: %s", hipGetErrorString(e));
+  }
+  st = run(1, 3, x, mask, norm_in_w, norm_in_b, p_in_w, p_in_b, g_in_w, g_in_b, norm_out_w,
+           norm_out_b, p_out_w, p_out_b, g_out_w, g_out_b, B, N, c_z, c, direction, eps, out,
+           workspace, workspace_bytes, cs);
+  const std::string run_err = g_err;
+  hipGraph_t g = nullptr;
+  e = hipStreamEndCapture(cs, &g);   // always end the capture, whatever run() returned
+  hipStreamDestroy(cs);
+  if (st != TRIMUL_OK) {
+    if (g) hipGraphDestroy(g);
+    return fail(st, "capture: %s", run_err.c_str());
+  }
+  if (e != hipSuccess || !g) return fail(TRIMUL_E_DEVICE, "hipStreamEndCapture: %s", hipGetErrorString(e));
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+  hipGraphDestroy(g);
+  if (e != hipSuccess) return fail(TRIMUL_E_DEVICE, "hipGraphInstantiate: %s", hipGetErrorString(e));
+  *graph = new trimul_graph_s{exec, dev};
+  return ok();
+}
+
+int trimul_graph_launch(trimul_graph_t graph, void* stream) {
+  if (!graph) return fail(TRIMUL_E_INVALID, "graph handle is NULL");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(TRIMUL_E_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev != graph->device)
+    return fail(TRIMUL_E_INVALID, "graph was created on device %d but device %d is current", graph->device, dev);
+  e = hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(TRIMUL_E_DEVICE, "hipGraphLaunch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int trimul_graph_destroy(trimul_graph_t graph) {
+  if (!graph) return ok();
+  hipError_t e = hipGraphExecDestroy(graph->exec);
+  delete graph;
+  if (e != hipSuccess) return fail(TRIMUL_E_DEVICE, "hipGraphExecDestroy: %s", hipGetErrorString(e));
+  return ok();
 }
 
 }  // extern "C"
