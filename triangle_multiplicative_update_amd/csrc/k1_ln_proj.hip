@@ -52,12 +52,17 @@ struct K1Smem {
   uint16_t z[2][K1_TP * ZP];
   uint16_t o[OB][2 * K1_GROUP * OP];
   float m[2][K1_TP];
+  float lnw[CZ], lnb[CZ];                  // LayerNorm_in affine, fp32 (c_z = 256 form)
 };
 
 template <int CZ>
 __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
   constexpr int NV = CZ / 64;      // 16-byte chunks of a pair row per lane
   constexpr int KS = CZ / 16;      // MFMA k-steps
+  // At c_z = 256 the 32 channels' weights alone take 128 registers: the
+  // LayerNorm parameters then live in LDS and the biases are kept as one
+  // scalar per lane (splat into the accumulator when a chain starts).
+  constexpr bool kWide = CZ > 128;
   using S = K1Smem<CZ>;
   __shared__ __attribute__((aligned(16))) S sm;
 
@@ -81,25 +86,34 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
   }
   // the biases enter as the accumulator input of the first MFMA of a chain
   // (every register of a lane's accumulator belongs to the lane's channel)
+  const float bias_vs = p.p_in_b ? bf16_to_f32(p.p_in_b[wrow]) : 0.0f;
+  const float bias_gs = p.g_in_b ? bf16_to_f32(p.g_in_b[wrow]) : 0.0f;
   f32x16 bias_v, bias_g;
-  {
-    const float bv = p.p_in_b ? bf16_to_f32(p.p_in_b[wrow]) : 0.0f;
-    const float bg = p.g_in_b ? bf16_to_f32(p.g_in_b[wrow]) : 0.0f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      bias_v[r] = bv;
-      bias_g[r] = bg;
-    }
+  for (int r = 0; r < 16; ++r) {
+    bias_v[r] = bias_vs;
+    bias_g[r] = bias_gs;
   }
+  auto splat = [](float v) {
+    f32x16 r;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) r[i] = v;
+    return r;
+  };
 
   // ---- LayerNorm lane mapping: pair `lp`, sub-lane `sub` ----
   const int lp = tid >> 3;
   const int sub = tid & 7;
   u32x4 lnw[NV], lnb[NV];
+  if constexpr (kWide) {
+    stage_f32(sm.lnw, p.ln_w, CZ);         // read after the prologue's first barrier
+    stage_f32(sm.lnb, p.ln_b, CZ);
+  } else {
 #pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    lnw[v] = ld16(p.ln_w + 8 * sub + 64 * v);
-    lnb[v] = ld16(p.ln_b + 8 * sub + 64 * v);
+    for (int v = 0; v < NV; ++v) {
+      lnw[v] = ld16(p.ln_w + 8 * sub + 64 * v);
+      lnb[v] = ld16(p.ln_b + 8 * sub + 64 * v);
+    }
   }
 
   const int N = p.N;
@@ -138,7 +152,8 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
     u32x4 xin[NV], z[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) xin[v] = xok ? xr[v] : u32x4{0, 0, 0, 0};
-    layer_norm_row<NV>(xin, lnw, lnb, p.eps, z);
+    if constexpr (kWide) layer_norm_row_lds<NV>(xin, sm.lnw, sm.lnb, sub, p.eps, z);
+    else layer_norm_row<NV>(xin, lnw, lnb, p.eps, z);
 #pragma unroll
     for (int v = 0; v < NV; ++v) st16(&sm.z[zb][lp * S::ZP + 8 * sub + 64 * v], z[v]);
     sm.m[zb][lp] = bf16_bits_late(mraw);   // the 8 lanes of a pair write the same value
@@ -161,8 +176,13 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
         for (int kk = 0; kk < KS / 4; ++kk) {
           const int ks = rg * (KS / 4) + kk;
           const bf16x8 a = ld_frag(&sm.z[zb][(32 * mb + l32) * S::ZP + 16 * ks + 8 * lhi]);
-          nv = mfma32x32x16(a, wv[ks], ks == 0 ? bias_v : nv);
-          ng = mfma32x32x16(a, wg[ks], ks == 0 ? bias_g : ng);
+          if constexpr (kWide) {
+            nv = mfma32x32x16(a, wv[ks], ks == 0 ? splat(bias_vs) : nv);
+            ng = mfma32x32x16(a, wg[ks], ks == 0 ? splat(bias_gs) : ng);
+          } else {
+            nv = mfma32x32x16(a, wv[ks], ks == 0 ? bias_v : nv);
+            ng = mfma32x32x16(a, wg[ks], ks == 0 ? bias_g : ng);
+          }
         }
       }
       const int m0 = 32 * emb + 8 * rg + 4 * lhi;   // first of 4 consecutive pairs
@@ -183,8 +203,13 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       const bf16x8 a = ld_frag(&sm.z[zb][(32 * mb + l32) * S::ZP + 16 * ks + 8 * lhi]);
-      nv = mfma32x32x16(a, wv[ks], ks == 0 ? bias_v : nv);
-      ng = mfma32x32x16(a, wg[ks], ks == 0 ? bias_g : ng);
+      if constexpr (kWide) {
+        nv = mfma32x32x16(a, wv[ks], ks == 0 ? splat(bias_vs) : nv);
+        ng = mfma32x32x16(a, wg[ks], ks == 0 ? splat(bias_gs) : ng);
+      } else {
+        nv = mfma32x32x16(a, wv[ks], ks == 0 ? bias_v : nv);
+        ng = mfma32x32x16(a, wg[ks], ks == 0 ? bias_g : ng);
+      }
     }
   };
 
@@ -213,6 +238,33 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
 
   int t = blockIdx.x;
   if (t >= ntiles) return;
+  if constexpr (kWide) {
+    // c_z = 256: the multiply dominates (four times the c = 128 work per
+    // pair) and the weights fill half the registers, so the tile runs one
+    // pair half at a time (one accumulator pair live): MFMAs then gate for
+    // half 0 and half 1, LayerNorm of the next tile, x loads two tiles
+    // ahead, one barrier, then the stores of this tile.
+    f32x16 av, ag;
+    fetch(t);
+    lds_barrier();           // LayerNorm parameters staged
+    ln_store(0);
+    if (t + stride < ntiles) fetch(t + stride);
+    lds_barrier();
+    int zb = 0, ob = 0;
+    for (; t < ntiles; t += stride) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        mma_only(zb, mb, av, ag);
+        half(std::false_type{}, 0, 0, av, ag, av, ag, zb, mb, ob, no_op);
+      }
+      if (t + stride < ntiles) ln_store(zb ^ 1);
+      if (t + 2 * stride < ntiles) fetch(t + 2 * stride);
+      lds_barrier();
+      store(t, ob);
+      ob ^= 1;
+      zb ^= 1;
+    }
+  } else {
   f32x16 v0, g0, v1, g1;   // accumulators of pair halves 0 and 1
 
   // prologue: LayerNorm of the first tile, x of the second in flight, the
@@ -269,6 +321,7 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
   tile(I2{}, std::false_type{}, std::false_type{});
   lds_barrier();
   store(t - stride, prev);
+  }
 }
 
 }  // namespace

@@ -37,6 +37,8 @@ struct K3Smem {
   uint8_t y[K3_TP * RB];                   // y, then u
   uint8_t z[K3_TP * RB];                   // z_in
   uint8_t o[K3_TP * RB];                   // out staging
+  // c = 256 form: LayerNorm affines and output biases as fp32
+  float inw[C], inb[C], outw[C], outb[C], bp[C], bg[C];
 };
 
 // byte offset of 16-byte slot `slot` of pair row `r` in a swizzled tile
@@ -55,6 +57,9 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   constexpr int NY = (C / 2) * 8 / K3_THREADS;   // (channel pair, 8-pair chunk) items per thread
   using S = K3Smem<C>;
   __shared__ __attribute__((aligned(16))) S sm;
+  // At c = 256 the 32 output channels' weights alone take 128 registers:
+  // the LayerNorm parameters and the output biases then live in LDS.
+  constexpr bool kWide = C > 128;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -74,23 +79,35 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   }
   // accumulator register r holds output channel 32*nb + 8*(r/4) + 4*lhi + r%4
   float bias_p[16], bias_g[16];
+  if constexpr (!kWide) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int n = 32 * nb + 8 * (r >> 2) + 4 * lhi + (r & 3);
-    bias_p[r] = p.p_out_b ? bf16_to_f32(p.p_out_b[n]) : 0.0f;
-    bias_g[r] = p.g_out_b ? bf16_to_f32(p.g_out_b[n]) : 0.0f;
+    for (int r = 0; r < 16; ++r) {
+      const int n = 32 * nb + 8 * (r >> 2) + 4 * lhi + (r & 3);
+      bias_p[r] = p.p_out_b ? bf16_to_f32(p.p_out_b[n]) : 0.0f;
+      bias_g[r] = p.g_out_b ? bf16_to_f32(p.g_out_b[n]) : 0.0f;
+    }
   }
 
   // ---- LayerNorm lane mapping (same as stage 1): pair lp, sub-lane sub ----
   const int lp = tid >> 3;
   const int sub = tid & 7;
   u32x4 inw[NV], inb[NV], outw[NV], outb[NV];
+  if constexpr (kWide) {
+    stage_f32(sm.inw, p.ln_in_w, CZ);
+    stage_f32(sm.inb, p.ln_in_b, CZ);
+    stage_f32(sm.outw, p.ln_out_w, C);
+    stage_f32(sm.outb, p.ln_out_b, C);
+    stage_f32(sm.bp, p.p_out_b, CZ);
+    stage_f32(sm.bg, p.g_out_b, CZ);
+    lds_barrier();
+  } else {
 #pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    inw[v] = ld16(p.ln_in_w + 8 * sub + 64 * v);
-    inb[v] = ld16(p.ln_in_b + 8 * sub + 64 * v);
-    outw[v] = ld16(p.ln_out_w + 8 * sub + 64 * v);
-    outb[v] = ld16(p.ln_out_b + 8 * sub + 64 * v);
+    for (int v = 0; v < NV; ++v) {
+      inw[v] = ld16(p.ln_in_w + 8 * sub + 64 * v);
+      inb[v] = ld16(p.ln_in_b + 8 * sub + 64 * v);
+      outw[v] = ld16(p.ln_out_w + 8 * sub + 64 * v);
+      outb[v] = ld16(p.ln_out_b + 8 * sub + 64 * v);
+    }
   }
 
   const int N = p.N;
@@ -98,35 +115,44 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
 
   // ---- register prefetch of one tile: y (channel pairs) and x ----
   u32x4 ya[NY], yb[NY], xr[NV];
-  auto prefetch = [&](int t) {
+  // y item: channel pair cp = id / 8, pair chunk jc = id % 8 (8 lanes cover one
+  // channel's 128 bytes)
+  auto load_y = [&](int t, int it) {
     const int row = t / p.nchunk;
     const int j0 = (t - row * p.nchunk) * K3_TP;
-    // y item: channel pair cp = id / 8, pair chunk jc = id % 8 (8 lanes cover one
-    // channel's 128 bytes)
-#pragma unroll
-    for (int it = 0; it < NY; ++it) {
-      const int id = it * K3_THREADS + tid;
-      const int cp = id >> 3;
-      const int jc = id & 7;
-      const uint16_t* src = p.plane_y + size_t(2 * cp) * ch_stride + size_t(row) * p.n_pad + j0 + 8 * jc;
-      ya[it] = ld16(src);
-      yb[it] = ld16(src + ch_stride);
-    }
+    const int id = it * K3_THREADS + tid;
+    const int cp = id >> 3;
+    const int jc = id & 7;
+    const uint16_t* src = p.plane_y + size_t(2 * cp) * ch_stride + size_t(row) * p.n_pad + j0 + 8 * jc;
+    ya[it] = ld16(src);
+    yb[it] = ld16(src + ch_stride);
+  };
+  auto load_x = [&](int t) {
+    const int row = t / p.nchunk;
+    const int j0 = (t - row * p.nchunk) * K3_TP;
     const bool valid = j0 + lp < N;
 #pragma unroll
     for (int v = 0; v < NV; ++v)
       xr[v] = valid ? ld16(p.x + (size_t(row) * N + j0 + lp) * CZ + 8 * sub + 64 * v) : u32x4{0, 0, 0, 0};
   };
+  auto prefetch = [&](int t) {
+#pragma unroll
+    for (int it = 0; it < NY; ++it) load_y(t, it);
+    load_x(t);
+  };
 
   int t = blockIdx.x;
-  if (t < p.ntiles) prefetch(t);
+  if (!kWide && t < p.ntiles) prefetch(t);
   for (; t < p.ntiles; t += gridDim.x) {
+    // c = 256: no registers to spare for a tile of lookahead; this tile's
+    // y items and x are loaded where they are used
     const int row = t / p.nchunk;                      // b * N + i
     const int j0 = (t - row * p.nchunk) * K3_TP;
 
     // ---- y -> pair-major LDS rows (two channels per dword) ----
 #pragma unroll
     for (int it = 0; it < NY; ++it) {
+      if constexpr (kWide) load_y(t, it);
       const int id = it * K3_THREADS + tid;
       const int cp = id >> 3;
       const int jc = id & 7;
@@ -142,9 +168,11 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
     }
     // ---- x -> LayerNorm_in -> z_in in LDS ----
     {
+      if constexpr (kWide) load_x(t);
       u32x4 z[NV];
       if (j0 + lp < N) {
-        layer_norm_row<NV>(xr, inw, inb, p.eps, z);
+        if constexpr (kWide) layer_norm_row_lds<NV>(xr, sm.inw, sm.inb, sub, p.eps, z);
+        else layer_norm_row<NV>(xr, inw, inb, p.eps, z);
       } else {
 #pragma unroll
         for (int v = 0; v < NV; ++v) z[v] = u32x4{0, 0, 0, 0};
@@ -155,14 +183,15 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
     lds_barrier();
 
     // ---- prefetch the next tile while this one is processed ----
-    if (t + gridDim.x < p.ntiles) prefetch(t + gridDim.x);
+    if (!kWide && t + gridDim.x < p.ntiles) prefetch(t + gridDim.x);
 
     // ---- LayerNorm_out in place on the pair rows of y ----
     {
       u32x4 yr[NV], u[NV];
 #pragma unroll
       for (int v = 0; v < NV; ++v) yr[v] = ld16(sm.y + soff<C>(lp, sub + 8 * v));
-      layer_norm_row<NV>(yr, outw, outb, p.eps, u);
+      if constexpr (kWide) layer_norm_row_lds<NV>(yr, sm.outw, sm.outb, sub, p.eps, u);
+      else layer_norm_row<NV>(yr, outw, outb, p.eps, u);
 #pragma unroll
       for (int v = 0; v < NV; ++v) st16(sm.y + soff<C>(lp, sub + 8 * v), u[v]);
     }
@@ -173,14 +202,37 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
     for (int jb = 0; jb < JOBS; ++jb) {
       const int mb = mb_first + jb;
       f32x16 acc_p, acc_g;
+      if constexpr (kWide) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        acc_p[r] = bias_p[r];
-        acc_g[r] = bias_g[r];
+        for (int q = 0; q < 4; ++q) {   // 4 consecutive output channels per register group
+          const int n = 32 * nb + 8 * q + 4 * lhi;
+          const f32x4 bp4 = *reinterpret_cast<const f32x4*>(&sm.bp[n]);
+          const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&sm.bg[n]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc_p[4 * q + e] = bp4[e];
+            acc_g[4 * q + e] = bg4[e];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          acc_p[r] = bias_p[r];
+          acc_g[r] = bias_g[r];
+        }
       }
-      const int prow = 32 * mb + l32;     // pair this lane feeds as the B operand
+      int prow = 32 * mb + l32;           // pair this lane feeds as the B operand
+      // c = 256: an opaque copy per tile, so the fragment addresses derived
+      // from it are not hoisted out of the tile loop (they would hold 64
+      // registers for the whole kernel)
+      if constexpr (kWide) asm volatile("" : "+v"(prow));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
+        // c = 256: keep the compiler from loading every k-step's fragments
+        // ahead (128 more registers); four k-steps in flight are enough
+        if constexpr (kWide) {
+          if (ks % 4 == 0 && ks > 0) asm volatile("" ::: "memory");
+        }
         const bf16x8 u = ld_frag(sm.y + soff<C>(prow, 2 * ks + lhi));
         const bf16x8 z = ld_frag(sm.z + soff<C>(prow, 2 * ks + lhi));
         acc_p = mfma32x32x16(wp[ks], u, acc_p);

@@ -110,19 +110,29 @@ __device__ __forceinline__ int lds_swz(int r) {
 // square root, affine after normalisation, result rounded once to bf16. The
 // stage-1 and stage-3 kernels both call this with the same lane mapping, so
 // stage 3's recomputed z_in has the bits stage 1 used.
-template <int NV>
-__device__ __forceinline__ void layer_norm_row(const u32x4 (&xin)[NV], const u32x4 (&w)[NV],
-                                               const u32x4 (&b)[NV], float eps, u32x4 (&zout)[NV]) {
+// Rows of 4 or more chunks per lane (c_z = 256) unpack the bf16 input again
+// in each pass instead of keeping 8 * NV floats live across the two
+// reductions; the values, and so the result bits, are the same either way.
+template <int NV, class WB>
+__device__ __forceinline__ void layer_norm_row_wb(const u32x4 (&xin)[NV], WB&& affine, float eps,
+                                                  u32x4 (&zout)[NV]) {
 #pragma clang fp contract(off)
   constexpr float inv_n = 1.0f / float(64 * NV);
-  float v[NV][8];
+  constexpr bool kKeep = NV <= 2;
+  float v[kKeep ? NV : 1][8];
+  auto elem = [&](int c, int e) -> float {
+    if constexpr (kKeep) return v[c][e];
+    else return (e & 1) ? bf16_hi(xin[c][e >> 1]) : bf16_lo(xin[c][e >> 1]);
+  };
+  if constexpr (kKeep) {
 #pragma unroll
-  for (int c = 0; c < NV; ++c) unpack8(xin[c], v[c]);
+    for (int c = 0; c < NV; ++c) unpack8(xin[c], v[c]);
+  }
   float s = 0.0f;
 #pragma unroll
   for (int c = 0; c < NV; ++c)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s = s + v[c][e];
+    for (int e = 0; e < 8; ++e) s = s + elem(c, e);
   s = sum_lanes8(s);
   const float mean = s * inv_n;
   float ss = 0.0f;
@@ -130,7 +140,7 @@ __device__ __forceinline__ void layer_norm_row(const u32x4 (&xin)[NV], const u32
   for (int c = 0; c < NV; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float d = v[c][e] - mean;
+      const float d = elem(c, e) - mean;
       ss = __builtin_fmaf(d, d, ss);
     }
   ss = sum_lanes8(ss);
@@ -139,14 +149,50 @@ __device__ __forceinline__ void layer_norm_row(const u32x4 (&xin)[NV], const u32
 #pragma unroll
   for (int c = 0; c < NV; ++c) {
     float wv[8], bv[8];
-    unpack8(w[c], wv);
-    unpack8(b[c], bv);
+    affine(c, wv, bv);
     float o[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf((v[c][e] - mean) * rstd, wv[e], bv[e]);
+    for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf((elem(c, e) - mean) * rstd, wv[e], bv[e]);
     zout[c] = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
                     pack_bf16x2(o[6], o[7])};
   }
+}
+
+// affine parameters held in registers as packed bf16 (chunk c of this lane)
+template <int NV>
+__device__ __forceinline__ void layer_norm_row(const u32x4 (&xin)[NV], const u32x4 (&w)[NV],
+                                               const u32x4 (&b)[NV], float eps, u32x4 (&zout)[NV]) {
+  layer_norm_row_wb<NV>(xin, [&](int c, float (&wv)[8], float (&bv)[8]) {
+    unpack8(w[c], wv);
+    unpack8(b[c], bv);
+  }, eps, zout);
+}
+
+// affine parameters as fp32 arrays in LDS (the full row; this lane reads the
+// 8 + 8 values of each of its chunks, the same for every pair): the same
+// arithmetic as the register form, for kernels without registers to spare
+template <int NV>
+__device__ __forceinline__ void layer_norm_row_lds(const u32x4 (&xin)[NV], const float* w, const float* b,
+                                                   int sub, float eps, u32x4 (&zout)[NV]) {
+  layer_norm_row_wb<NV>(xin, [&](int c, float (&wv)[8], float (&bv)[8]) {
+    const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + 8 * sub + 64 * c);
+    const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + 8 * sub + 64 * c + 4);
+    const f32x4 b0 = *reinterpret_cast<const f32x4*>(b + 8 * sub + 64 * c);
+    const f32x4 b1 = *reinterpret_cast<const f32x4*>(b + 8 * sub + 64 * c + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      wv[e] = w0[e];
+      wv[4 + e] = w1[e];
+      bv[e] = b0[e];
+      bv[4 + e] = b1[e];
+    }
+  }, eps, zout);
+}
+
+// Widen a bf16 vector of length n into an fp32 LDS array (block-cooperative;
+// the caller synchronises before the first read). A NULL source gives zeros.
+__device__ __forceinline__ void stage_f32(float* dst, const uint16_t* src, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) dst[i] = src ? bf16_to_f32(src[i]) : 0.0f;
 }
 
 // ------------------------------------------------------------- sigmoid -----
