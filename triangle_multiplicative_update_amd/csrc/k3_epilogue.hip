@@ -19,7 +19,9 @@
 // bit-identical -> LDS; LayerNorm_out in place on the y rows; MFMA 32x32x16
 // with D[out channel][pair] for the value and the gate; sigmoid * value in
 // fp32 -> bf16 -> LDS [pair][channel] -> 16-byte coalesced stores of out.
-// All pair-major LDS tiles use the 256-byte-row slot swizzle (lds_swz).
+// The y/u and z tiles use the 256-byte-row slot swizzle (lds_swz); the out
+// staging tile has its own 8-byte-unit swizzle (ooff), both conflict-free for
+// their accesses under gfx950's LDS bank model.
 
 #include "trimul_device.hpp"
 #include "trimul_kernels.hpp"
@@ -47,6 +49,14 @@ __device__ __forceinline__ int soff(int r, int slot) {
   return r * (C * 2) + ((slot ^ lds_swz(r)) << 4);
 }
 
+// Out staging: 8-byte unit u of pair row r at unit u ^ (r % 32). The epilogue
+// writes 32 rows x one unit per 8-byte instruction (32 distinct units: no
+// conflict); the store pass reads 16-byte chunk c of row r from chunk
+// c ^ ((r % 32) >> 1), with its two 8-byte halves swapped when r is odd.
+template <int C>
+__device__ __forceinline__ int ooff(int r, int unit) {
+  return r * (C * 2) + ((unit ^ (r & 31)) << 3);
+}
 template <int C>
 __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   constexpr int CZ = C;                    // c_z == c
@@ -245,7 +255,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) o[q] = sigmoid_f(acc_g[4 * rg + q]) * acc_p[4 * rg + q];
         const u32x2 packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        *reinterpret_cast<u32x2*>(sm.o + soff<C>(prow, 4 * nb + rg) + 8 * lhi) = packed;
+        *reinterpret_cast<u32x2*>(sm.o + ooff<C>(prow, 2 * (4 * nb + rg) + lhi)) = packed;
       }
     }
     lds_barrier();
@@ -257,7 +267,11 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
       const int pr = id / (CZ / 8);
       const int cc = id - pr * (CZ / 8);
       if (j0 + pr < N)
-        st16(p.out + (size_t(row) * N + j0 + pr) * CZ + 8 * cc, ld16(sm.o + soff<C>(pr, cc)));
+      {
+        u32x4 v = ld16(sm.o + pr * (C * 2) + ((cc ^ ((pr & 31) >> 1)) << 4));
+        if (pr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        st16(p.out + (size_t(row) * N + j0 + pr) * CZ + 8 * cc, v);
+      }
     }
   }
 }

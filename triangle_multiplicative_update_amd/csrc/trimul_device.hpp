@@ -91,15 +91,25 @@ __device__ __forceinline__ float sum_lanes8(float v) {
 
 // ------------------------------------------------------- LDS swizzle ----
 //
-// Pair-major LDS tiles use rows of 256 B per 128 channels (no padding) and
-// place the 16-byte slot `s` of row `r` at slot s ^ lds_swz(r). With 64
-// four-byte banks (one 256-byte line per bank cycle) this keeps three access
-// patterns free of bank conflicts: 16 consecutive rows read at one slot (MFMA
-// fragments), 2 rows x 8 slots read as 16-byte vectors (LayerNorm lanes), and
-// the transposing dword writes of 8 rows {8j + e} x 8 consecutive dwords.
+// LDS bank model of gfx950, measured (per-instruction throughput of
+// ds_read/ds_write patterns at 8 waves per CU): 64 banks of 4 bytes (one
+// 256-byte line per cycle). A 16-byte access runs in 4 cycles of 16 lanes,
+// the cycle of lane l being (bit 5 of l, parity of bits 2..4 of l): lanes
+// 0-3, 12-15, 20-23, 24-27 share one cycle, 4-7, 8-11, 16-19, 28-31 the next,
+// and likewise in the upper half. An 8-byte access runs in 2 cycles of 32
+// lanes, the cycle being the parity of lane bits 5 and 1. Within a cycle the
+// lanes must hit distinct banks (identical addresses excepted).
+//
+// Pair-major tiles with 256-byte rows (128 bf16 channels) place 16-byte slot
+// `s` of row `r` at slot s ^ lds_swz(r), with the row bits XOR-ed in as
+// bit 0 -> 1, bit 1 -> 8, bit 3 -> 2, bit 4 -> 4, bit 5 -> 8 (bit 2 -> 0). Under
+// the model this keeps every access of the stage-3 tiles conflict-free: the
+// MFMA fragment reads (32 consecutive rows at one slot, the upper half at the
+// next slot), the LayerNorm rows (8 lanes x 16 bytes per row, 8 rows), and the
+// transposing 4-byte writes of 8 rows {8j + e} x 8 consecutive dwords (found
+// by exhaustive search over such linear swizzles, checked on the GPU).
 __device__ __forceinline__ int lds_swz(int r) {
-  return (((r >> 0) & 1) << 3) ^ ((r >> 1) & 1) ^ (((r >> 2) & 1) << 2) ^ (((r >> 3) & 1) << 1) ^
-         (((r >> 4) & 1) << 2) ^ (((r >> 5) & 1) << 3);
+  return ((r & 1) ? 1 : 0) ^ ((r & 2) ? 8 : 0) ^ ((r & 8) ? 2 : 0) ^ ((r & 16) ? 4 : 0) ^ ((r & 32) ? 8 : 0);
 }
 
 // ------------------------------------------------------------ LayerNorm ----
