@@ -65,3 +65,20 @@ def test_scaled_inputs_sigma2(gpu):
     wl = si.custom(1, 160, 128, x_std=2.0, mask="padded", mask_len=140, seed=77)
     inp = si.generate(wl)
     _run_and_check(inp, "outgoing", wl.name, gpu)
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_fractional_mask(gpu, direction):
+    # Page section "Mathematics and numerics": a and b are sigmoid(g) v m for the
+    # mask value m, whatever it is; the served envelope takes any real mask cast
+    # once to bf16. Values in (0, 1), above 1, negative, +0.0 and -0.0.
+    wl = si.custom(1, 96, 128, mask="bernoulli", seed=4242)
+    inp = si.generate(wl)
+    rng = np.random.default_rng(99)
+    m = rng.uniform(-0.5, 1.5, size=(1, 96, 96)).astype(np.float32)
+    m[rng.random(size=m.shape) < 0.1] = 0.0
+    m[rng.random(size=m.shape) < 0.05] = -0.0
+    m[rng.random(size=m.shape) < 0.2] = 1.0
+    inp = dict(inp)
+    inp["mask"] = (m.view(np.uint32) >> 16).astype(np.uint16)   # exact: truncation, then used as given
+    _run_and_check(inp, direction, "b1_n96_c128_fractional", gpu)

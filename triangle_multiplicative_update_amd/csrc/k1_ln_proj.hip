@@ -51,7 +51,9 @@ struct K1Smem {
   static constexpr int OB = CZ == 128 ? 3 : 2;   // output staging buffers
   uint16_t z[2][K1_TP * ZP];
   uint16_t o[OB][2 * K1_GROUP * OP];
-  float m[2][K1_TP];
+  float mb[2][K1_TP];                      // per pair: +inf for m = 0, else 0
+  float mi[2][K1_TP];                      // per pair: 1 / m, or 1 for m = 0
+  float m[2][K1_TP];                       // per pair: m (c_z = 256 form)
   float lnw[CZ], lnb[CZ];                  // LayerNorm_in affine, fp32 (c_z = 256 form)
 };
 
@@ -127,9 +129,9 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
   const int mask_step = p.mask ? 1 : 0;
 
   // x and mask of this lane's LayerNorm pair in tile t, as loaded; pairs past
-  // N read a valid pair's x (zeroed when LayerNorm consumes it) and the mask
-  // constant 0. No instruction uses the loaded values before LayerNorm, so
-  // nothing waits for the loads until then.
+  // N read a valid pair's x and the mask constant 0 (their a and b are then
+  // +0.0 whatever their z). No instruction uses the loaded values before
+  // LayerNorm, so nothing waits for the loads until then.
   u32x4 xr[NV];
   uint16_t mraw = 0;
   bool xok = false;
@@ -147,16 +149,33 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
     mraw = ld_global_u16(xok ? mask + pi * mask_step : kMaskConst + 1);
   };
 
-  // LayerNorm_in of the fetched tile -> z (bf16) and mask in LDS buffer `zb`
+  // LayerNorm_in of the fetched tile -> z (bf16) and mask terms in LDS buffer
+  // `zb`. The mask enters the gate as sigmoid(g) v m = v / ((1 + 2^t) / m)
+  // with t = -g log2 e: a pair with m = 0 gets t = +inf (so 1 / inf = 0 and
+  // the final fma with +0.0 gives exactly +0.0), any other m the factor 1 / m
+  // in the denominator (1 / 1 = 1 exactly, so m = 1 costs no rounding).
   auto ln_store = [&](int zb) {
-    u32x4 xin[NV], z[NV];
+    u32x4 z[NV];
+    if constexpr (kWide) {
+      // (zeroing the x of pairs past N keeps this form's register
+      // allocation free of spills)
+      u32x4 xin[NV];
 #pragma unroll
-    for (int v = 0; v < NV; ++v) xin[v] = xok ? xr[v] : u32x4{0, 0, 0, 0};
-    if constexpr (kWide) layer_norm_row_lds<NV>(xin, sm.lnw, sm.lnb, sub, p.eps, z);
-    else layer_norm_row<NV>(xin, lnw, lnb, p.eps, z);
+      for (int v = 0; v < NV; ++v) xin[v] = xok ? xr[v] : u32x4{0, 0, 0, 0};
+      layer_norm_row_lds<NV>(xin, sm.lnw, sm.lnb, sub, p.eps, z);
+    } else {
+      layer_norm_row<NV>(xr, lnw, lnb, p.eps, z);
+    }
 #pragma unroll
     for (int v = 0; v < NV; ++v) st16(&sm.z[zb][lp * S::ZP + 8 * sub + 64 * v], z[v]);
-    sm.m[zb][lp] = bf16_bits_late(mraw);   // the 8 lanes of a pair write the same value
+    const float m = bf16_bits_late(mraw);  // the 8 lanes of a pair write the same values
+    if constexpr (kWide) {
+      sm.m[zb][lp] = m;
+    } else {
+      const bool off = m == 0.0f;
+      sm.mb[zb][lp] = off ? __builtin_inff() : 0.0f;
+      sm.mi[zb][lp] = off ? 1.0f : __builtin_amdgcn_rcpf(m);
+    }
   };
 
   // One overlapped half step. With DO_MMA: the 2 * KS MFMAs of pair half
@@ -186,12 +205,23 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
         }
       }
       const int m0 = 32 * emb + 8 * rg + 4 * lhi;   // first of 4 consecutive pairs
-      const f32x4 mm = *reinterpret_cast<const f32x4*>(&sm.m[ezb][m0]);
       float o[4];
+      if constexpr (kWide) {
+        // (no registers to spare for the two mask terms at c_z = 256)
+        const f32x4 mm = *reinterpret_cast<const f32x4*>(&sm.m[ezb][m0]);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int r = 4 * rg + q;
-        o[q] = __builtin_fmaf(sigmoid_f(eg[r]) * ev[r], mm[q], 0.0f);   // +0.0 for m = 0
+        for (int q = 0; q < 4; ++q) {
+          const int r = 4 * rg + q;
+          o[q] = __builtin_fmaf(sigmoid_f(eg[r]) * ev[r], mm[q], 0.0f);   // +0.0 for m = 0
+        }
+      } else {
+        const f32x4 mb = *reinterpret_cast<const f32x4*>(&sm.mb[ezb][m0]);
+        const f32x4 mi = *reinterpret_cast<const f32x4*>(&sm.mi[ezb][m0]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r = 4 * rg + q;
+          o[q] = gate_masked(eg[r], ev[r], mb[q], mi[q]);
+        }
       }
       const u32x2 packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
       *reinterpret_cast<u32x2*>(&sm.o[ob][(plane * K1_GROUP + chs + l32) * S::OP + m0]) = packed;
@@ -217,18 +247,41 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
   // (128 a + 128 b channels) x 64 pairs, one 16-byte chunk per thread and
   // part `it` (0..3); n_pad is a multiple of 64, so every chunk of the tile
   // lies inside its row
+  // Buffer stores: a lane's byte offset inside a tile (channel row and
+  // chunk) is the same for every tile and sits in a register; the tile's
+  // (row, first pair) offset is uniform and goes in the scalar offset. Every
+  // plane is below 2^31 bytes (the extent rule), so 32-bit offsets suffice.
   constexpr int kStoreParts = (2 * K1_GROUP * K1_TP / 8) / K1_THREADS;
+  static_assert(kStoreParts == 4 && K1_THREADS / 8 * 2 == K1_GROUP, "parts 0-1: plane a, 2-3: plane b");
+  const uint32_t plane_bytes = uint32_t(ch_stride) * uint32_t(p.c) * 2u;
+  const auto rsrc_a = __builtin_amdgcn_make_buffer_rsrc(p.plane_a, 0, plane_bytes, 0x00020000);
+  const auto rsrc_b = __builtin_amdgcn_make_buffer_rsrc(p.plane_b, 0, plane_bytes, 0x00020000);
+  auto lane_off = [&](int it) {
+    const int srow = (it * K1_THREADS + tid) >> 3;   // staging row: plane * 128 + channel
+    const int gch = group * K1_GROUP + (srow & (K1_GROUP - 1));
+    return (uint32_t(gch) * uint32_t(ch_stride) + 8u * uint32_t(tid & 7)) * 2u;
+  };
+  // c_z = 128 keeps the four offsets in registers; c_z = 256 has none to
+  // spare and recomputes them per store (as a global store)
+  uint32_t st_off[kStoreParts];
+  if constexpr (!kWide) {
+#pragma unroll
+    for (int it = 0; it < kStoreParts; ++it) st_off[it] = lane_off(it);
+  }
   auto store_part = [&](int t, int ob, int it) {
     const int row = t / nchunk;
     const int inner0 = (t - row * nchunk) * K1_TP;
-    const int id = it * K1_THREADS + tid;
-    const int srow = id >> 3;              // staging row: plane * 128 + channel
-    const int c16 = id & 7;
-    const int pl = srow / K1_GROUP;
-    const int gch = group * K1_GROUP + (srow - pl * K1_GROUP);
-    uint16_t* dst = (pl ? p.plane_b : p.plane_a) + size_t(gch) * ch_stride + size_t(row) * p.n_pad +
-                    inner0 + 8 * c16;
-    st16(dst, ld16(&sm.o[ob][srow * S::OP + 8 * c16]));
+    const int srow = (it * K1_THREADS + tid) >> 3;
+    const int c16 = tid & 7;
+    const int soff = __builtin_amdgcn_readfirstlane((row * p.n_pad + inner0) * 2);
+    const u32x4 v = ld16(&sm.o[ob][srow * S::OP + 8 * c16]);
+    if constexpr (kWide) {
+      const int gch = group * K1_GROUP + (srow & (K1_GROUP - 1));
+      st16((it < 2 ? p.plane_a : p.plane_b) + size_t(gch) * ch_stride + size_t(row) * p.n_pad + inner0 + 8 * c16,
+           v);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b128(v, it < 2 ? rsrc_a : rsrc_b, st_off[it], soff, 0);
+    }
   };
   auto store = [&](int t, int ob) {
 #pragma unroll

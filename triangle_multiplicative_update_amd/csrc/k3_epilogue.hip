@@ -123,6 +123,33 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   const int N = p.N;
   const size_t ch_stride = size_t(p.B) * N * p.n_pad;
 
+  // c = 128 addresses through buffer resources: a lane's offset inside a
+  // tile is fixed (registers), the tile's base is uniform (scalar offset).
+  // Every plane and x/out are below 2^31 bytes (the extent rule), so 32-bit
+  // offsets suffice. A load past the end of x returns zeros and a store at an
+  // offset past the end is dropped by the hardware.
+  const uint32_t xo_bytes = uint32_t(p.B) * uint32_t(N) * uint32_t(N) * uint32_t(CZ) * 2u;
+  const auto rsrc_y = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.plane_y), 0, uint32_t(ch_stride) * uint32_t(C) * 2u,
+                                                        0x00020000);
+  const auto rsrc_x = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x), 0, xo_bytes, 0x00020000);
+  const auto rsrc_o = __builtin_amdgcn_make_buffer_rsrc(p.out, 0, xo_bytes, 0x00020000);
+  constexpr int NST = (K3_TP * CZ / 8) / K3_THREADS;   // 16-byte out chunks per thread per tile
+  uint32_t y_off[NY], o_off[NST];
+  uint32_t x_off = 0;
+  if constexpr (!kWide) {
+#pragma unroll
+    for (int it = 0; it < NY; ++it) {
+      const int id = it * K3_THREADS + tid;
+      y_off[it] = (2u * uint32_t(id >> 3) * uint32_t(ch_stride) + 8u * uint32_t(id & 7)) * 2u;
+    }
+#pragma unroll
+    for (int it = 0; it < NST; ++it) {
+      const int id = it * K3_THREADS + tid;
+      o_off[it] = uint32_t(id) * 16u;   // pair id / (CZ / 8), chunk id % (CZ / 8)
+    }
+    x_off = (uint32_t(lp) * CZ + 8u * uint32_t(sub)) * 2u;
+  }
+
   // ---- register prefetch of one tile: y (channel pairs) and x ----
   u32x4 ya[NY], yb[NY], xr[NV];
   // y item: channel pair cp = id / 8, pair chunk jc = id % 8 (8 lanes cover one
@@ -130,6 +157,12 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   auto load_y = [&](int t, int it) {
     const int row = t / p.nchunk;
     const int j0 = (t - row * p.nchunk) * K3_TP;
+    if constexpr (!kWide) {
+      const int so = __builtin_amdgcn_readfirstlane((row * p.n_pad + j0) * 2);
+      ya[it] = buffer_load16(rsrc_y, y_off[it], so);
+      yb[it] = buffer_load16(rsrc_y, y_off[it], so + int(ch_stride) * 2);
+      return;
+    }
     const int id = it * K3_THREADS + tid;
     const int cp = id >> 3;
     const int jc = id & 7;
@@ -140,6 +173,14 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   auto load_x = [&](int t) {
     const int row = t / p.nchunk;
     const int j0 = (t - row * p.nchunk) * K3_TP;
+    if constexpr (!kWide) {
+      // pairs past N read the next row's x (or zeros past the end); their
+      // outputs are never stored
+      const int so = __builtin_amdgcn_readfirstlane((row * N + j0) * CZ * 2);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) xr[v] = buffer_load16(rsrc_x, x_off + 128u * v, so);
+      return;
+    }
     const bool valid = j0 + lp < N;
 #pragma unroll
     for (int v = 0; v < NV; ++v)
@@ -169,8 +210,8 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t a = ya[it][q], b = yb[it][q];
-        const uint32_t even = (a & 0xffffu) | (b << 16);          // pair 8jc + 2q
-        const uint32_t odd = (a >> 16) | (b & 0xffff0000u);       // pair 8jc + 2q + 1
+        const uint32_t even = __builtin_amdgcn_perm(b, a, 0x05040100u);   // pair 8jc + 2q
+        const uint32_t odd = __builtin_amdgcn_perm(b, a, 0x07060302u);    // pair 8jc + 2q + 1
         const int r0 = 8 * jc + 2 * q;
         *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0, cp >> 2) + 4 * (cp & 3)) = even;
         *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0 + 1, cp >> 2) + 4 * (cp & 3)) = odd;
@@ -180,12 +221,15 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
     {
       if constexpr (kWide) load_x(t);
       u32x4 z[NV];
-      if (j0 + lp < N) {
-        if constexpr (kWide) layer_norm_row_lds<NV>(xr, sm.inw, sm.inb, sub, p.eps, z);
-        else layer_norm_row<NV>(xr, inw, inb, p.eps, z);
-      } else {
+      if constexpr (kWide) {
+        if (j0 + lp < N) {
+          layer_norm_row_lds<NV>(xr, sm.inw, sm.inb, sub, p.eps, z);
+        } else {
 #pragma unroll
-        for (int v = 0; v < NV; ++v) z[v] = u32x4{0, 0, 0, 0};
+          for (int v = 0; v < NV; ++v) z[v] = u32x4{0, 0, 0, 0};
+        }
+      } else {
+        layer_norm_row<NV>(xr, inw, inb, p.eps, z);   // every lane: no branch
       }
 #pragma unroll
       for (int v = 0; v < NV; ++v) st16(sm.z + soff<C>(lp, sub + 8 * v), z[v]);
@@ -262,15 +306,23 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
 
     // ---- coalesced pair-major stores of out ----
 #pragma unroll
-    for (int it = 0; it < (K3_TP * CZ / 8) / K3_THREADS; ++it) {
+    for (int it = 0; it < NST; ++it) {
       const int id = it * K3_THREADS + tid;
       const int pr = id / (CZ / 8);
       const int cc = id - pr * (CZ / 8);
-      if (j0 + pr < N)
-      {
+      if constexpr (kWide) {
+        if (j0 + pr < N) {
+          u32x4 v = ld16(sm.o + pr * (C * 2) + ((cc ^ ((pr & 31) >> 1)) << 4));
+          if (pr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+          st16(p.out + (size_t(row) * N + j0 + pr) * CZ + 8 * cc, v);
+        }
+      } else {
         u32x4 v = ld16(sm.o + pr * (C * 2) + ((cc ^ ((pr & 31) >> 1)) << 4));
         if (pr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        st16(p.out + (size_t(row) * N + j0 + pr) * CZ + 8 * cc, v);
+        // a pair past N gets an offset past the end of out: the store is dropped
+        const int so = __builtin_amdgcn_readfirstlane((row * N + j0) * CZ * 2);
+        const uint32_t off = (j0 + pr < N) ? o_off[it] : 0x80000000u;
+        buffer_store16(rsrc_o, v, off, so);
       }
     }
   }

@@ -40,6 +40,14 @@ __device__ __forceinline__ void unpack8(const u32x4& c, float (&v)[8]) {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// 16-byte buffer load / store at byte offset voff + soff (soff uniform)
+__device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, const u32x4& v, uint32_t voff, int soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+}
 __device__ __forceinline__ bf16x8 ld_frag(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // One bf16 from global memory. The address-space cast makes it a global load:
@@ -211,6 +219,16 @@ __device__ __forceinline__ void stage_f32(float* dst, const uint16_t* src, int n
 __device__ __forceinline__ float sigmoid_f(float g) {
   const float e = __builtin_amdgcn_exp2f(g * -1.4426950408889634f);
   return __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+// sigmoid(g) * v * m with the mask folded into the exponent and denominator:
+// v / ((1 + 2^t) * mi) with t = -g log2 e + mb, where (mb, mi) = (+inf, 1)
+// for m = 0 and (0, 1/m) otherwise. m = 0 gives 2^inf = inf, 1 / inf = 0 and
+// fma(v, 0, +0.0) = +0.0 exactly; m = 1 gives the same bits as
+// sigmoid_f(g) * v. The final fma with +0.0 turns a -0.0 product into +0.0.
+__device__ __forceinline__ float gate_masked(float g, float v, float mb, float mi) {
+  const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(g, -1.4426950408889634f, mb));
+  return __builtin_fmaf(v, __builtin_amdgcn_rcpf(__builtin_fmaf(e, mi, mi)), 0.0f);
 }
 
 // ---------------------------------------------------------------- MFMA -----
