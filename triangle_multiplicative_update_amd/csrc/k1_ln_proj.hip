@@ -51,9 +51,12 @@ struct K1Smem {
   static constexpr int OB = CZ == 128 ? 3 : 2;   // output staging buffers
   uint16_t z[2][K1_TP * ZP];
   uint16_t o[OB][2 * K1_GROUP * OP];
-  float mb[2][K1_TP];                      // per pair: +inf for m = 0, else 0
-  float mi[2][K1_TP];                      // per pair: 1 / m, or 1 for m = 0
-  float m[2][K1_TP];                       // per pair: m (c_z = 256 form)
+  // mask terms per pair, c_z = 128 form: three buffers, because the gate of
+  // a tile's second pair half runs after the tile's barrier and the next
+  // tile writes the mask terms of the tile after it before its own barrier
+  float mb[3][K1_TP];                      // +inf for m = 0, else 0
+  float mi[3][K1_TP];                      // 1 / m, or 1 for m = 0
+  float m[2][K1_TP];                       // m (c_z = 256 form: tile-sequential, two suffice)
   float lnw[CZ], lnb[CZ];                  // LayerNorm_in affine, fp32 (c_z = 256 form)
 };
 
@@ -149,12 +152,12 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
     mraw = ld_global_u16(xok ? mask + pi * mask_step : kMaskConst + 1);
   };
 
-  // LayerNorm_in of the fetched tile -> z (bf16) and mask terms in LDS buffer
-  // `zb`. The mask enters the gate as sigmoid(g) v m = v / ((1 + 2^t) / m)
+  // LayerNorm_in of the fetched tile -> z (bf16) in LDS buffer `zb` and the
+  // mask terms in mask buffer `mz`. The mask enters the gate as sigmoid(g) v m = v / ((1 + 2^t) / m)
   // with t = -g log2 e: a pair with m = 0 gets t = +inf (so 1 / inf = 0 and
   // the final fma with +0.0 gives exactly +0.0), any other m the factor 1 / m
   // in the denominator (1 / 1 = 1 exactly, so m = 1 costs no rounding).
-  auto ln_store = [&](int zb) {
+  auto ln_store = [&](int zb, int mz) {
     u32x4 z[NV];
     if constexpr (kWide) {
       // (zeroing the x of pairs past N keeps this form's register
@@ -170,22 +173,22 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
     for (int v = 0; v < NV; ++v) st16(&sm.z[zb][lp * S::ZP + 8 * sub + 64 * v], z[v]);
     const float m = bf16_bits_late(mraw);  // the 8 lanes of a pair write the same values
     if constexpr (kWide) {
-      sm.m[zb][lp] = m;
+      sm.m[mz][lp] = m;
     } else {
       const bool off = m == 0.0f;
-      sm.mb[zb][lp] = off ? __builtin_inff() : 0.0f;
-      sm.mi[zb][lp] = off ? 1.0f : __builtin_amdgcn_rcpf(m);
+      sm.mb[mz][lp] = off ? __builtin_inff() : 0.0f;
+      sm.mi[mz][lp] = off ? 1.0f : __builtin_amdgcn_rcpf(m);
     }
   };
 
   // One overlapped half step. With DO_MMA: the 2 * KS MFMAs of pair half
   // `mb` of the tile in z buffer `zb` into (nv, ng). Interleaved with them:
-  // sigmoid(eg) * ev * mask for pair half `emb` of the tile whose mask is in
-  // buffer `ezb`, rounded to bf16 and staged channel-major in output buffer
+  // sigmoid(eg) * ev * mask for pair half `emb` of the tile whose mask terms
+  // are in mask buffer `emz`, rounded to bf16 and staged channel-major in output buffer
   // `ob`. The accumulator layout puts 4 consecutive pairs of one channel in
   // each register group, i.e. 8 contiguous bytes of a staging row.
   auto half = [&](auto do_mma, int zb, int mb, f32x16& nv, f32x16& ng, const f32x16& ev,
-                  const f32x16& eg, int ezb, int emb, int ob, auto&& each_rg) {
+                  const f32x16& eg, int emz, int emb, int ob, auto&& each_rg) {
     constexpr bool kMma = decltype(do_mma)::value;
 #pragma unroll
     for (int rg = 0; rg < 4; ++rg) {
@@ -208,15 +211,15 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
       float o[4];
       if constexpr (kWide) {
         // (no registers to spare for the two mask terms at c_z = 256)
-        const f32x4 mm = *reinterpret_cast<const f32x4*>(&sm.m[ezb][m0]);
+        const f32x4 mm = *reinterpret_cast<const f32x4*>(&sm.m[emz][m0]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = 4 * rg + q;
           o[q] = __builtin_fmaf(sigmoid_f(eg[r]) * ev[r], mm[q], 0.0f);   // +0.0 for m = 0
         }
       } else {
-        const f32x4 mb = *reinterpret_cast<const f32x4*>(&sm.mb[ezb][m0]);
-        const f32x4 mi = *reinterpret_cast<const f32x4*>(&sm.mi[ezb][m0]);
+        const f32x4 mb = *reinterpret_cast<const f32x4*>(&sm.mb[emz][m0]);
+        const f32x4 mi = *reinterpret_cast<const f32x4*>(&sm.mi[emz][m0]);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int r = 4 * rg + q;
@@ -287,6 +290,19 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
 #pragma unroll
     for (int it = 0; it < kStoreParts; ++it) store_part(t, ob, it);
   };
+  // Vector-memory operations retire in issue order, so a wait for the x and
+  // mask loads of a later tile is a count of what was issued after them: the
+  // previous tile's plane stores. The compiler takes that count once per loop
+  // and merges the paths into the loop, so every path must issue the same
+  // number of stores after the loads, or the wait falls back to draining the
+  // stores. Where there is no previous tile, these stores stand in: their
+  // offset lies past the end of plane a, so the hardware drops them.
+  // (distinct offsets, so the compiler does not merge them)
+  auto no_store = [&](int it) { __builtin_amdgcn_raw_buffer_store_b32(0u, rsrc_a, 0x80000000u + 16u * it, 0, 0); };
+  auto no_stores = [&]() {
+#pragma unroll
+    for (int it = 0; it < kStoreParts; ++it) no_store(it);
+  };
   auto no_op = [](int) {};
 
   int t = blockIdx.x;
@@ -300,8 +316,9 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
     f32x16 av, ag;
     fetch(t);
     lds_barrier();           // LayerNorm parameters staged
-    ln_store(0);
+    ln_store(0, 0);
     if (t + stride < ntiles) fetch(t + stride);
+    no_stores();
     lds_barrier();
     int zb = 0, ob = 0;
     for (; t < ntiles; t += stride) {
@@ -310,7 +327,7 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
         mma_only(zb, mb, av, ag);
         half(std::false_type{}, 0, 0, av, ag, av, ag, zb, mb, ob, no_op);
       }
-      if (t + stride < ntiles) ln_store(zb ^ 1);
+      if (t + stride < ntiles) ln_store(zb ^ 1, zb ^ 1);
       if (t + 2 * stride < ntiles) fetch(t + 2 * stride);
       lds_barrier();
       store(t, ob);
@@ -323,8 +340,9 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
   // prologue: LayerNorm of the first tile, x of the second in flight, the
   // MFMAs of the first tile's half 0
   fetch(t);
-  ln_store(0);
+  ln_store(0, 0);
   if (t + stride < ntiles) fetch(t + stride);
+  no_stores();
   lds_barrier();
   mma_only(0, 0, v0, g0);
 
@@ -333,14 +351,15 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
   // previous tile, 1 = one store part per register group of the overlapped
   // half step (the stores trickle out between the MFMAs instead of stalling
   // every wave at once), 2 = whole store if prev >= 0 (the last tiles).
-  int zb = 0, ob = 0, prev = -1;
+  int zb = 0, ob = 0, prev = -1, mz = 0;   // mz: mask buffer of tile t
   auto tile = [&](auto store_mode, auto has_next, auto has_next2) {
     constexpr int kStore = decltype(store_mode)::value;
     constexpr bool kNext = decltype(has_next)::value;
     constexpr bool kNext2 = decltype(has_next2)::value;
     // half 1's MFMAs || half 0's gate epilogue
-    half(std::true_type{}, zb, 1, v1, g1, v0, g0, zb, 0, ob, no_op);
-    if constexpr (kNext) ln_store(zb ^ 1);
+    const int mz_next = mz == 2 ? 0 : mz + 1;
+    half(std::true_type{}, zb, 1, v1, g1, v0, g0, mz, 0, ob, no_op);
+    if constexpr (kNext) ln_store(zb ^ 1, mz_next);
     if constexpr (kNext2) fetch(t + 2 * stride);
     lds_barrier();
     if constexpr (kStore == 2) {
@@ -355,13 +374,16 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
     auto st = [&](int rg) {
       if constexpr (kStore == 1 && S::OB != 2) {
         if (rg < kStoreParts) store_part(tp, pb, rg);
+      } else if constexpr (kStore == 0) {
+        if (rg < kStoreParts) no_store(rg);
       }
     };
-    if constexpr (kNext) half(std::true_type{}, zb ^ 1, 0, v0, g0, v1, g1, zb, 1, ob, st);
-    else half(std::false_type{}, 0, 0, v0, g0, v1, g1, zb, 1, ob, st);
+    if constexpr (kNext) half(std::true_type{}, zb ^ 1, 0, v0, g0, v1, g1, mz, 1, ob, st);
+    else half(std::false_type{}, 0, 0, v0, g0, v1, g1, mz, 1, ob, st);
     prev = ob;
     ob = (ob + 1 == S::OB) ? 0 : ob + 1;
     zb ^= 1;
+    mz = mz_next;
     t += stride;
   };
   using I0 = std::integral_constant<int, 0>;

@@ -194,6 +194,17 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
 
   int t = blockIdx.x;
   if (!kWide && t < p.ntiles) prefetch(t);
+  if constexpr (!kWide) {
+    // Vector-memory operations retire in issue order, so the wait for the
+    // prefetched y and x of a tile is a count of what was issued after them:
+    // the previous tile's out stores. The compiler merges the paths into the
+    // loop, so the path from here must issue as many stores after the
+    // prefetch, or every tile's wait drains the previous tile's stores. These
+    // have offsets past the end of out: the hardware drops them (distinct
+    // offsets, so the compiler does not merge them).
+#pragma unroll
+    for (int it = 0; it < NST; ++it) __builtin_amdgcn_raw_buffer_store_b32(0u, rsrc_o, 0x80000000u + 16u * it, 0, 0);
+  }
   for (; t < p.ntiles; t += gridDim.x) {
     // c = 256: no registers to spare for a tile of lookahead; this tile's
     // y items and x are loaded where they are used
