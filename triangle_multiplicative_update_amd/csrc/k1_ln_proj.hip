@@ -228,6 +228,17 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
       }
       const u32x2 packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
       *reinterpret_cast<u32x2*>(&sm.o[ob][(plane * K1_GROUP + chs + l32) * S::OP + m0]) = packed;
+      if constexpr (kMma && !kWide) {
+        // scheduling hint for the register group: its four LDS reads first,
+        // then each MFMA followed by three VALU instructions (measured best
+        // of 3, 5 and 8; the MFMAs otherwise issue in a burst)
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+        }
+      }
     }
   };
 
