@@ -339,13 +339,278 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// c = 128: wave-specialised form. Waves 0-3 ("matrix waves") each own one
+// 32-channel output block for both pair halves: the p_out and g_out MFMAs, the
+// gate, the out staging and the stores. Waves 4-7 ("LayerNorm waves") load y
+// and x, transpose y to pair-major rows and run LayerNorm_out and
+// LayerNorm_in (the stage-1 lane mapping: 8 lanes per pair, so z_in is
+// bit-identical), 16 pairs per wave, writing u and z for the matrix waves.
+// Each SIMD holds one wave of each kind, so the matrix cores of one overlap
+// the vector ALU work of the other. Iteration k has two barriers:
+//   phase 1: LayerNorm waves transpose the y of tile k+1 (in registers) into
+//            the shared y rows (each load instruction read whole 128-byte
+//            lines) and write z of tile k+1 (LayerNorm_in needs only x);
+//            matrix waves run tile k's MFMAs (u/z buffer k % 2) and the
+//            first pair half's gate
+//   phase 2: LayerNorm waves write u of tile k+1 and load y and x of tile
+//            k + 3 (two register sets: a tile's loads have 1.5 iterations to
+//            land); matrix waves run the second half's gate and store tile
+//            k - 1.
+// The matrix waves never wait for the transposes: their inputs were complete
+// an iteration earlier, so their work spans both phases.
+constexpr int K3W_PAIRS = 16;              // pairs per LayerNorm wave
+
+struct K3WsSmem {
+  static constexpr int RB = 256;           // pair row bytes (128 bf16)
+  uint8_t u[2][K3_TP * RB];                // LayerNorm_out rows
+  uint8_t z[2][K3_TP * RB];                // LayerNorm_in rows
+  uint8_t o[2][K3_TP * RB];                // out staging
+  uint8_t y[K3_TP * RB];                   // transposed y rows of the next tile
+};
+
+__global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
+  constexpr int C = 128, CZ = 128;
+  constexpr int NV = C / 64;               // LayerNorm chunks per lane
+  constexpr int KS = C / 16;               // MFMA k-steps
+  constexpr int NY = (C / 2) * 8 / 256;    // (channel pair, 8-pair chunk) items per LayerNorm lane
+  using S = K3WsSmem;
+  __shared__ __attribute__((aligned(16))) S sm;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int lhi = lane >> 5;
+
+  const int N = p.N;
+  const size_t ch_stride = size_t(p.B) * N * p.n_pad;
+  const uint32_t xo_bytes = uint32_t(p.B) * uint32_t(N) * uint32_t(N) * uint32_t(CZ) * 2u;
+  const int G = gridDim.x;
+  const int nk = int(blockIdx.x) < p.ntiles ? (p.ntiles - int(blockIdx.x) + G - 1) / G : 0;
+  if (nk == 0) return;                      // the whole block: no barrier is left unmatched
+  // iterations 0 .. nk do work; both kinds of wave run an even count (one
+  // idle iteration at most), so the LayerNorm waves' loop, unrolled by two,
+  // has no path that skips half of its body and its loads
+  const int nit = (nk + 2) & ~1;
+  auto tile_at = [&](int k, int& row, int& j0) {
+    const int t = int(blockIdx.x) + k * G;
+    row = t / p.nchunk;                     // b * N + i
+    j0 = (t - row * p.nchunk) * K3_TP;
+  };
+
+  if (wave < 4) {
+    // ---- matrix wave: output channels 32 * nb .. 32 * nb + 31 ----
+    const int nb = wave;
+    const int nrow = 32 * nb + l32;
+    bf16x8 wp[KS], wg[KS];
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      wp[ks] = ld_frag(p.p_out + size_t(nrow) * C + 16 * ks + 8 * lhi);
+      wg[ks] = ld_frag(p.g_out + size_t(nrow) * CZ + 16 * ks + 8 * lhi);
+    }
+    // accumulator register r holds output channel 32*nb + 8*(r/4) + 4*lhi + r%4
+    f32x16 bias_p, bias_g;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int n = 32 * nb + 8 * (r >> 2) + 4 * lhi + (r & 3);
+      bias_p[r] = p.p_out_b ? bf16_to_f32(p.p_out_b[n]) : 0.0f;
+      bias_g[r] = p.g_out_b ? bf16_to_f32(p.g_out_b[n]) : 0.0f;
+    }
+    const auto rsrc_o = __builtin_amdgcn_make_buffer_rsrc(p.out, 0, xo_bytes, 0x00020000);
+    constexpr int NST = (K3_TP * CZ / 8) / 256;   // 16-byte out chunks per matrix-wave lane
+    auto mma = [&](int b, int mb, f32x16& acc_p, f32x16& acc_g) {
+      const int prow = 32 * mb + l32;       // pair this lane feeds as the B operand
+      acc_p = bias_p;
+      acc_g = bias_g;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 u = ld_frag(sm.u[b] + soff<C>(prow, 2 * ks + lhi));
+        const bf16x8 z = ld_frag(sm.z[b] + soff<C>(prow, 2 * ks + lhi));
+        acc_p = mfma32x32x16(wp[ks], u, acc_p);
+        acc_g = mfma32x32x16(wg[ks], z, acc_g);
+      }
+    };
+    auto gate = [&](int b, int mb, const f32x16& acc_p, const f32x16& acc_g) {
+      const int prow = 32 * mb + l32;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        float o[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = sigmoid_f(acc_g[4 * rg + q]) * acc_p[4 * rg + q];
+        const u32x2 packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        *reinterpret_cast<u32x2*>(sm.o[b] + ooff<C>(prow, 2 * (4 * nb + rg) + lhi)) = packed;
+      }
+    };
+    auto store = [&](int k) {
+      // ---- pair-major stores of tile k from out buffer k % 2 ----
+      int row, j0;
+      tile_at(k, row, j0);
+      const int so = __builtin_amdgcn_readfirstlane((row * N + j0) * CZ * 2);
+      const uint8_t* ob = sm.o[k & 1];
+#pragma unroll
+      for (int it = 0; it < NST; ++it) {
+        const int id = it * 256 + tid;
+        const int pr = id / (CZ / 8);
+        const int cc = id - pr * (CZ / 8);
+        u32x4 v = ld16(ob + pr * (C * 2) + ((cc ^ ((pr & 31) >> 1)) << 4));
+        if (pr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        // a pair past N gets an offset past the end of out: the store is dropped
+        const uint32_t off = (j0 + pr < N) ? uint32_t(id) * 16u : 0x80000000u;
+        buffer_store16(rsrc_o, v, off, so);
+      }
+    };
+    lds_barrier();                           // the LayerNorm waves' first tile: y rows
+    lds_barrier();                           // ... and u, z
+    for (int k = 0; k < nit; ++k) {
+      const int b = k & 1;
+      f32x16 p0, g0, p1, g1;
+      if (k < nk) {
+        // the second half's MFMAs overlap the first half's gate
+        mma(b, 0, p0, g0);
+        mma(b, 1, p1, g1);
+        gate(b, 0, p0, g0);
+      }
+      lds_barrier();
+      if (k < nk) gate(b, 1, p1, g1);
+      if (k >= 1 && k <= nk) store(k - 1);
+      lds_barrier();
+    }
+  } else {
+    // ---- LayerNorm wave lw: transposes its share of y, normalises pairs 16 lw .. 16 lw + 15 ----
+    const int lw = wave - 4;
+    const int ltid = tid - 256;
+    const int sub = lane & 7;                // sub-lane of a pair (stage-1 mapping)
+    const int pl = lane >> 3;                // pair within a pass of 8
+    u32x4 inw[NV], inb[NV], outw[NV], outb[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      inw[v] = ld16(p.ln_in_w + 8 * sub + 64 * v);
+      inb[v] = ld16(p.ln_in_b + 8 * sub + 64 * v);
+      outw[v] = ld16(p.ln_out_w + 8 * sub + 64 * v);
+      outb[v] = ld16(p.ln_out_b + 8 * sub + 64 * v);
+    }
+    const auto rsrc_y = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.plane_y), 0,
+                                                          uint32_t(ch_stride) * uint32_t(C) * 2u, 0x00020000);
+    const auto rsrc_x = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x), 0, xo_bytes, 0x00020000);
+    // y item it: channel pair cp = id / 8 (channels 2 cp, 2 cp + 1), 8-pair
+    // chunk jc = id % 8 (8 lanes read one channel's 128 bytes)
+    uint32_t y_off[NY];
+#pragma unroll
+    for (int it = 0; it < NY; ++it) {
+      const int id = it * 256 + ltid;
+      y_off[it] = (2u * uint32_t(id >> 3) * uint32_t(ch_stride) + 8u * uint32_t(id & 7)) * 2u;
+    }
+    // x: pass q, pair 16 lw + 8 q + pl, sub-lane sub
+    const uint32_t x_off = (uint32_t(K3W_PAIRS * lw + pl) * CZ + 8u * uint32_t(sub)) * 2u;
+    const int ych = int(ch_stride) * 2;      // bytes from channel 2 cp to 2 cp + 1
+    u32x4 yas[2][NY], ybs[2][NY], xrs[2][2][NV];   // two register sets
+    // Loads are unconditional (a tile past the block's last loads the last
+    // one again): a conditional load would leave the compiler merging two
+    // versions of the registers with copies, and each copy of a register
+    // still being loaded waits for every load in flight.
+    auto prefetch = [&](int k, auto set) {
+      constexpr int e = decltype(set)::value;
+      auto& ya = yas[e];
+      auto& yb = ybs[e];
+      auto& xr = xrs[e];
+      int row, j0;
+      tile_at(min(k, nk - 1), row, j0);
+      const int sy = __builtin_amdgcn_readfirstlane((row * p.n_pad + j0) * 2);
+      const int sx = __builtin_amdgcn_readfirstlane((row * N + j0) * CZ * 2);
+#pragma unroll
+      for (int it = 0; it < NY; ++it) {
+        ya[it] = buffer_load16(rsrc_y, y_off[it], sy);
+        yb[it] = buffer_load16(rsrc_y, y_off[it], sy + ych);
+      }
+      // pairs past N read the next row's x (or zeros past the end); their
+      // outputs are never stored
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) xr[q][v] = buffer_load16(rsrc_x, x_off + 2048u * q + 128u * v, sx);
+    };
+    auto transpose = [&](auto set) {
+      constexpr int e = decltype(set)::value;
+      const auto& ya = yas[e];
+      const auto& yb = ybs[e];
+#pragma unroll
+      for (int it = 0; it < NY; ++it) {
+        const int id = it * 256 + ltid;
+        const int cp = id >> 3;
+        const int jc = id & 7;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int r0 = 8 * jc + 2 * q;
+          const uint32_t even = __builtin_amdgcn_perm(yb[it][q], ya[it][q], 0x05040100u);   // pair r0
+          const uint32_t odd = __builtin_amdgcn_perm(yb[it][q], ya[it][q], 0x07060302u);    // pair r0 + 1
+          *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0, cp >> 2) + 4 * (cp & 3)) = even;
+          *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0 + 1, cp >> 2) + 4 * (cp & 3)) = odd;
+        }
+      }
+    };
+    auto ln_in = [&](int b, auto set) {
+      constexpr int e = decltype(set)::value;
+      const auto& xr = xrs[e];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int P = K3W_PAIRS * lw + 8 * q + pl;   // pair within the tile
+        u32x4 z[NV];
+        layer_norm_row<NV>(xr[q], inw, inb, p.eps, z);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) st16(sm.z[b] + soff<C>(P, sub + 8 * v), z[v]);
+      }
+    };
+    auto ln_out = [&](int b) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int P = K3W_PAIRS * lw + 8 * q + pl;
+        u32x4 yr[NV], u[NV];
+#pragma unroll
+        for (int v = 0; v < NV; ++v) yr[v] = ld16(sm.y + soff<C>(P, sub + 8 * v));
+        layer_norm_row<NV>(yr, outw, outb, p.eps, u);
+#pragma unroll
+        for (int v = 0; v < NV; ++v) st16(sm.u[b] + soff<C>(P, sub + 8 * v), u[v]);
+      }
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    // tile k lives in register set k % 2
+    prefetch(0, I0{});
+    prefetch(1, I1{});
+    transpose(I0{});
+    ln_in(0, I0{});
+    lds_barrier();
+    ln_out(0);
+    prefetch(2, I0{});
+    lds_barrier();
+    // iteration k works on tile k + 1 (set (k + 1) % 2) and refills that set
+    // with tile k + 3
+    auto iteration = [&](int k, auto set) {
+      if (k + 1 < nk) {
+        transpose(set);
+        ln_in((k + 1) & 1, set);
+      }
+      lds_barrier();
+      if (k + 1 < nk) ln_out((k + 1) & 1);
+      prefetch(k + 3, set);
+      lds_barrier();
+    };
+    for (int k = 0; k < nit; k += 2) {
+      iteration(k, I1{});
+      iteration(k + 1, I0{});
+    }
+  }
+}
+
 }  // namespace
 
 int k3_tiles(int B, int N) { return B * N * ((N + K3_TP - 1) / K3_TP); }
 
 hipError_t launch_k3(const K3Args& a, int grid_x, hipStream_t stream) {
   if (a.c == 128) {
-    hipLaunchKernelGGL(k3_epilogue<128>, dim3(grid_x), dim3(K3_THREADS), 0, stream, a);
+    hipLaunchKernelGGL(k3_epilogue_ws, dim3(grid_x), dim3(K3_THREADS), 0, stream, a);
   } else if (a.c == 256) {
     hipLaunchKernelGGL(k3_epilogue<256>, dim3(grid_x), dim3(K3_THREADS), 0, stream, a);
   } else {
