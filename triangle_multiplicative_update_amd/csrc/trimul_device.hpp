@@ -126,6 +126,7 @@ __device__ __forceinline__ int lds_swz(int r) {
 // holds the NV chunks starting at element 8*sub + 64*v. Statistics in fp32,
 // two passes (mean, then mean of squared deviations, biased), eps inside the
 // square root, affine after normalisation, result rounded once to bf16. The
+// summation order is fixed (partial sums, then the 8-lane reduction). The
 // stage-1 and stage-3 kernels both call this with the same lane mapping, so
 // stage 3's recomputed z_in has the bits stage 1 used.
 // Rows of 4 or more chunks per lane (c_z = 256) unpack the bf16 input again
@@ -146,21 +147,30 @@ __device__ __forceinline__ void layer_norm_row_wb(const u32x4 (&xin)[NV], WB&& a
 #pragma unroll
     for (int c = 0; c < NV; ++c) unpack8(xin[c], v[c]);
   }
-  float s = 0.0f;
-#pragma unroll
-  for (int c = 0; c < NV; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) s = s + elem(c, e);
-  s = sum_lanes8(s);
-  const float mean = s * inv_n;
-  float ss = 0.0f;
+  // in-lane sums as four interleaved partial sums (element i into sum i % 4),
+  // combined pairwise: dependency chains of 4 + 2 instead of 16, which a
+  // single wave per SIMD can issue without stalling
+  float sp[4];
 #pragma unroll
   for (int c = 0; c < NV; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float d = elem(c, e) - mean;
-      ss = __builtin_fmaf(d, d, ss);
+      const int i = 8 * c + e;
+      sp[i & 3] = (i < 4) ? elem(c, e) : sp[i & 3] + elem(c, e);
     }
+  float s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+  s = sum_lanes8(s);
+  const float mean = s * inv_n;
+  float ssp[4];
+#pragma unroll
+  for (int c = 0; c < NV; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = 8 * c + e;
+      const float d = elem(c, e) - mean;
+      ssp[i & 3] = (i < 4) ? d * d : __builtin_fmaf(d, d, ssp[i & 3]);
+    }
+  float ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);
   ss = sum_lanes8(ss);
   const float var = ss * inv_n;
   const float rstd = __builtin_amdgcn_rsqf(var + eps);
