@@ -29,6 +29,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,8 +50,11 @@ def kernel_sha(stage: int) -> str:
 
 
 def stage_of(kernel_name: str):
+    """Stage (1, 2, 3) of a kernel name as rocprofv3 prints it, e.g.
+    ``void trimul::k2_contract<256, ...>(trimul::K2Args)`` or
+    ``trimul::(anonymous namespace)::k3_epilogue_ws(trimul::K3Args)``."""
     for s, n in KERNEL_NAMES.items():
-        if n + "<" in kernel_name:
+        if re.search(r"\b" + n + r"(<|_ws\b|\()", kernel_name):
             return s
     return None
 
