@@ -9,19 +9,18 @@
 // channel-major, out leaves pair-major.
 //
 // Work decomposition. A tile is 64 pairs (b, i, j0..j0+63): one 128-byte row
-// of each y plane and 64 contiguous pair rows of x and out. A persistent
-// block of 8 waves keeps the output weights in registers: each wave owns 32
-// output channels (p_out and g_out rows) and one or both 32-pair halves.
-//
-// Per tile: y (c channels x 64 pairs, prefetched one tile ahead) is
-// transposed to pair-major LDS rows by packing two channels per dword; x
-// (prefetched) -> LayerNorm_in with the stage-1 lane mapping, so z_in is
-// bit-identical -> LDS; LayerNorm_out in place on the y rows; MFMA 32x32x16
-// with D[out channel][pair] for the value and the gate; sigmoid * value in
-// fp32 -> bf16 -> LDS [pair][channel] -> 16-byte coalesced stores of out.
-// The y/u and z tiles use the 256-byte-row slot swizzle (lds_swz); the out
-// staging tile has its own 8-byte-unit swizzle (ooff), both conflict-free for
-// their accesses under gfx950's LDS bank model.
+// of each y plane and 64 contiguous pair rows of x and out; blocks of 8 waves
+// are persistent. Two forms: at c = 128 the waves specialise (k3_epilogue_ws:
+// four matrix waves, four LayerNorm waves, one of each per SIMD); at c = 256
+// every wave runs every phase (k3_epilogue<256>). Both transpose y to
+// pair-major LDS rows two channels per dword, run LayerNorm_in with the
+// stage-1 lane mapping (so z_in is bit-identical) and LayerNorm_out, compute
+// the value and gate with MFMA 32x32x16 as D[out channel][pair] (weights as
+// the A operand, held in registers), and stage sigmoid * value as bf16 in LDS
+// [pair][channel] for 16-byte coalesced stores. The y/u and z tiles use the
+// 256-byte-row slot swizzle (lds_swz); the out staging tile has its own
+// 8-byte-unit swizzle (ooff), both conflict-free for their accesses under
+// gfx950's LDS bank model.
 
 #include "trimul_device.hpp"
 #include "trimul_kernels.hpp"
@@ -39,8 +38,7 @@ struct K3Smem {
   uint8_t y[K3_TP * RB];                   // y, then u
   uint8_t z[K3_TP * RB];                   // z_in
   uint8_t o[K3_TP * RB];                   // out staging
-  // c = 256 form: LayerNorm affines and output biases as fp32
-  float inw[C], inb[C], outw[C], outb[C], bp[C], bg[C];
+  float inw[C], inb[C], outw[C], outb[C], bp[C], bg[C];   // LayerNorm affines, output biases
 };
 
 // byte offset of 16-byte slot `slot` of pair row `r` in a swizzled tile
@@ -57,19 +55,27 @@ template <int C>
 __device__ __forceinline__ int ooff(int r, int unit) {
   return r * (C * 2) + ((unit ^ (r & 31)) << 3);
 }
+
+// c = 256 form. Every wave runs every phase of a tile: y is loaded and
+// transposed to pair-major LDS rows two channels per dword, x is loaded and
+// LayerNorm_in (stage-1 lane mapping) writes z, LayerNorm_out runs in place on
+// the y rows, then each wave computes two (32-channel block, pair half) jobs
+// of the output projection and gate, and the tile is stored pair-major. The
+// 32 output channels' weights of a wave take 128 registers, so the LayerNorm
+// affines and the output biases live in LDS as fp32 and nothing is prefetched
+// a tile ahead.
 template <int C>
 __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
+  static_assert(C == 256, "the c = 128 form is k3_epilogue_ws");
   constexpr int CZ = C;                    // c_z == c
   constexpr int NV = C / 64;               // LayerNorm chunks per lane
   constexpr int KS = C / 16;               // MFMA k-steps
   constexpr int NB = CZ / 32;              // 32-channel output blocks
   constexpr int JOBS = 2 * NB / 8;         // (channel block, pair half) jobs per wave
   constexpr int NY = (C / 2) * 8 / K3_THREADS;   // (channel pair, 8-pair chunk) items per thread
+  constexpr int NST = (K3_TP * CZ / 8) / K3_THREADS;   // 16-byte out chunks per thread per tile
   using S = K3Smem<C>;
   __shared__ __attribute__((aligned(16))) S sm;
-  // At c = 256 the 32 output channels' weights alone take 128 registers:
-  // the LayerNorm parameters and the output biases then live in LDS.
-  constexpr bool kWide = C > 128;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -77,9 +83,8 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
 
-  // ---- wave job: output channel block nb, pair halves mb ----
-  const int nb = (JOBS == 1) ? (wave % NB) : wave;
-  const int mb_first = (JOBS == 1) ? (wave / NB) : 0;
+  // ---- wave jobs: output channel block nb, both pair halves ----
+  const int nb = wave;
   const int nrow = 32 * nb + l32;          // weight row (output channel) this lane feeds
   bf16x8 wp[KS], wg[KS];
 #pragma unroll
@@ -87,176 +92,69 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
     wp[ks] = ld_frag(p.p_out + size_t(nrow) * C + 16 * ks + 8 * lhi);
     wg[ks] = ld_frag(p.g_out + size_t(nrow) * CZ + 16 * ks + 8 * lhi);
   }
-  // accumulator register r holds output channel 32*nb + 8*(r/4) + 4*lhi + r%4
-  float bias_p[16], bias_g[16];
-  if constexpr (!kWide) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int n = 32 * nb + 8 * (r >> 2) + 4 * lhi + (r & 3);
-      bias_p[r] = p.p_out_b ? bf16_to_f32(p.p_out_b[n]) : 0.0f;
-      bias_g[r] = p.g_out_b ? bf16_to_f32(p.g_out_b[n]) : 0.0f;
-    }
-  }
 
   // ---- LayerNorm lane mapping (same as stage 1): pair lp, sub-lane sub ----
   const int lp = tid >> 3;
   const int sub = tid & 7;
-  u32x4 inw[NV], inb[NV], outw[NV], outb[NV];
-  if constexpr (kWide) {
-    stage_f32(sm.inw, p.ln_in_w, CZ);
-    stage_f32(sm.inb, p.ln_in_b, CZ);
-    stage_f32(sm.outw, p.ln_out_w, C);
-    stage_f32(sm.outb, p.ln_out_b, C);
-    stage_f32(sm.bp, p.p_out_b, CZ);
-    stage_f32(sm.bg, p.g_out_b, CZ);
-    lds_barrier();
-  } else {
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      inw[v] = ld16(p.ln_in_w + 8 * sub + 64 * v);
-      inb[v] = ld16(p.ln_in_b + 8 * sub + 64 * v);
-      outw[v] = ld16(p.ln_out_w + 8 * sub + 64 * v);
-      outb[v] = ld16(p.ln_out_b + 8 * sub + 64 * v);
-    }
-  }
+  stage_f32(sm.inw, p.ln_in_w, CZ);
+  stage_f32(sm.inb, p.ln_in_b, CZ);
+  stage_f32(sm.outw, p.ln_out_w, C);
+  stage_f32(sm.outb, p.ln_out_b, C);
+  stage_f32(sm.bp, p.p_out_b, CZ);
+  stage_f32(sm.bg, p.g_out_b, CZ);
+  lds_barrier();
 
   const int N = p.N;
   const size_t ch_stride = size_t(p.B) * N * p.n_pad;
 
-  // c = 128 addresses through buffer resources: a lane's offset inside a
-  // tile is fixed (registers), the tile's base is uniform (scalar offset).
-  // Every plane and x/out are below 2^31 bytes (the extent rule), so 32-bit
-  // offsets suffice. A load past the end of x returns zeros and a store at an
-  // offset past the end is dropped by the hardware.
-  const uint32_t xo_bytes = uint32_t(p.B) * uint32_t(N) * uint32_t(N) * uint32_t(CZ) * 2u;
-  const auto rsrc_y = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.plane_y), 0, uint32_t(ch_stride) * uint32_t(C) * 2u,
-                                                        0x00020000);
-  const auto rsrc_x = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x), 0, xo_bytes, 0x00020000);
-  const auto rsrc_o = __builtin_amdgcn_make_buffer_rsrc(p.out, 0, xo_bytes, 0x00020000);
-  constexpr int NST = (K3_TP * CZ / 8) / K3_THREADS;   // 16-byte out chunks per thread per tile
-  uint32_t y_off[NY], o_off[NST];
-  uint32_t x_off = 0;
-  if constexpr (!kWide) {
-#pragma unroll
-    for (int it = 0; it < NY; ++it) {
-      const int id = it * K3_THREADS + tid;
-      y_off[it] = (2u * uint32_t(id >> 3) * uint32_t(ch_stride) + 8u * uint32_t(id & 7)) * 2u;
-    }
-#pragma unroll
-    for (int it = 0; it < NST; ++it) {
-      const int id = it * K3_THREADS + tid;
-      o_off[it] = uint32_t(id) * 16u;   // pair id / (CZ / 8), chunk id % (CZ / 8)
-    }
-    x_off = (uint32_t(lp) * CZ + 8u * uint32_t(sub)) * 2u;
-  }
-
-  // ---- register prefetch of one tile: y (channel pairs) and x ----
-  u32x4 ya[NY], yb[NY], xr[NV];
-  // y item: channel pair cp = id / 8, pair chunk jc = id % 8 (8 lanes cover one
-  // channel's 128 bytes)
-  auto load_y = [&](int t, int it) {
-    const int row = t / p.nchunk;
-    const int j0 = (t - row * p.nchunk) * K3_TP;
-    if constexpr (!kWide) {
-      const int so = __builtin_amdgcn_readfirstlane((row * p.n_pad + j0) * 2);
-      ya[it] = buffer_load16(rsrc_y, y_off[it], so);
-      yb[it] = buffer_load16(rsrc_y, y_off[it], so + int(ch_stride) * 2);
-      return;
-    }
-    const int id = it * K3_THREADS + tid;
-    const int cp = id >> 3;
-    const int jc = id & 7;
-    const uint16_t* src = p.plane_y + size_t(2 * cp) * ch_stride + size_t(row) * p.n_pad + j0 + 8 * jc;
-    ya[it] = ld16(src);
-    yb[it] = ld16(src + ch_stride);
-  };
-  auto load_x = [&](int t) {
-    const int row = t / p.nchunk;
-    const int j0 = (t - row * p.nchunk) * K3_TP;
-    if constexpr (!kWide) {
-      // pairs past N read the next row's x (or zeros past the end); their
-      // outputs are never stored
-      const int so = __builtin_amdgcn_readfirstlane((row * N + j0) * CZ * 2);
-#pragma unroll
-      for (int v = 0; v < NV; ++v) xr[v] = buffer_load16(rsrc_x, x_off + 128u * v, so);
-      return;
-    }
-    const bool valid = j0 + lp < N;
-#pragma unroll
-    for (int v = 0; v < NV; ++v)
-      xr[v] = valid ? ld16(p.x + (size_t(row) * N + j0 + lp) * CZ + 8 * sub + 64 * v) : u32x4{0, 0, 0, 0};
-  };
-  auto prefetch = [&](int t) {
-#pragma unroll
-    for (int it = 0; it < NY; ++it) load_y(t, it);
-    load_x(t);
-  };
-
-  int t = blockIdx.x;
-  if (!kWide && t < p.ntiles) prefetch(t);
-  if constexpr (!kWide) {
-    // Vector-memory operations retire in issue order, so the wait for the
-    // prefetched y and x of a tile is a count of what was issued after them:
-    // the previous tile's out stores. The compiler merges the paths into the
-    // loop, so the path from here must issue as many stores after the
-    // prefetch, or every tile's wait drains the previous tile's stores. These
-    // have offsets past the end of out: the hardware drops them (distinct
-    // offsets, so the compiler does not merge them).
-#pragma unroll
-    for (int it = 0; it < NST; ++it) __builtin_amdgcn_raw_buffer_store_b32(0u, rsrc_o, 0x80000000u + 16u * it, 0, 0);
-  }
-  for (; t < p.ntiles; t += gridDim.x) {
-    // c = 256: no registers to spare for a tile of lookahead; this tile's
-    // y items and x are loaded where they are used
+  for (int t = blockIdx.x; t < p.ntiles; t += gridDim.x) {
     const int row = t / p.nchunk;                      // b * N + i
     const int j0 = (t - row * p.nchunk) * K3_TP;
 
     // ---- y -> pair-major LDS rows (two channels per dword) ----
+    // item: channel pair cp = id / 8, pair chunk jc = id % 8 (8 lanes cover
+    // one channel's 128 bytes)
 #pragma unroll
     for (int it = 0; it < NY; ++it) {
-      if constexpr (kWide) load_y(t, it);
       const int id = it * K3_THREADS + tid;
       const int cp = id >> 3;
       const int jc = id & 7;
+      const uint16_t* src = p.plane_y + size_t(2 * cp) * ch_stride + size_t(row) * p.n_pad + j0 + 8 * jc;
+      const u32x4 ya = ld16(src);
+      const u32x4 yb = ld16(src + ch_stride);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const uint32_t a = ya[it][q], b = yb[it][q];
-        const uint32_t even = __builtin_amdgcn_perm(b, a, 0x05040100u);   // pair 8jc + 2q
-        const uint32_t odd = __builtin_amdgcn_perm(b, a, 0x07060302u);    // pair 8jc + 2q + 1
+        const uint32_t even = __builtin_amdgcn_perm(yb[q], ya[q], 0x05040100u);   // pair 8jc + 2q
+        const uint32_t odd = __builtin_amdgcn_perm(yb[q], ya[q], 0x07060302u);    // pair 8jc + 2q + 1
         const int r0 = 8 * jc + 2 * q;
         *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0, cp >> 2) + 4 * (cp & 3)) = even;
         *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0 + 1, cp >> 2) + 4 * (cp & 3)) = odd;
       }
     }
-    // ---- x -> LayerNorm_in -> z_in in LDS ----
+    // ---- x -> LayerNorm_in -> z_in in LDS (pairs past N: zeros) ----
     {
-      if constexpr (kWide) load_x(t);
-      u32x4 z[NV];
-      if constexpr (kWide) {
-        if (j0 + lp < N) {
-          layer_norm_row_lds<NV>(xr, sm.inw, sm.inb, sub, p.eps, z);
-        } else {
+      const bool valid = j0 + lp < N;
+      u32x4 xr[NV], z[NV];
 #pragma unroll
-          for (int v = 0; v < NV; ++v) z[v] = u32x4{0, 0, 0, 0};
-        }
+      for (int v = 0; v < NV; ++v)
+        xr[v] = valid ? ld16(p.x + (size_t(row) * N + j0 + lp) * CZ + 8 * sub + 64 * v) : u32x4{0, 0, 0, 0};
+      if (valid) {
+        layer_norm_row_lds<NV>(xr, sm.inw, sm.inb, sub, p.eps, z);
       } else {
-        layer_norm_row<NV>(xr, inw, inb, p.eps, z);   // every lane: no branch
+#pragma unroll
+        for (int v = 0; v < NV; ++v) z[v] = u32x4{0, 0, 0, 0};
       }
 #pragma unroll
       for (int v = 0; v < NV; ++v) st16(sm.z + soff<C>(lp, sub + 8 * v), z[v]);
     }
     lds_barrier();
 
-    // ---- prefetch the next tile while this one is processed ----
-    if (!kWide && t + gridDim.x < p.ntiles) prefetch(t + gridDim.x);
-
     // ---- LayerNorm_out in place on the pair rows of y ----
     {
       u32x4 yr[NV], u[NV];
 #pragma unroll
       for (int v = 0; v < NV; ++v) yr[v] = ld16(sm.y + soff<C>(lp, sub + 8 * v));
-      if constexpr (kWide) layer_norm_row_lds<NV>(yr, sm.outw, sm.outb, sub, p.eps, u);
-      else layer_norm_row<NV>(yr, outw, outb, p.eps, u);
+      layer_norm_row_lds<NV>(yr, sm.outw, sm.outb, sub, p.eps, u);
 #pragma unroll
       for (int v = 0; v < NV; ++v) st16(sm.y + soff<C>(lp, sub + 8 * v), u[v]);
     }
@@ -264,40 +162,29 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
 
     // ---- output projection and gate: D[out channel][pair] ----
 #pragma unroll
-    for (int jb = 0; jb < JOBS; ++jb) {
-      const int mb = mb_first + jb;
+    for (int mb = 0; mb < JOBS; ++mb) {
       f32x16 acc_p, acc_g;
-      if constexpr (kWide) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {   // 4 consecutive output channels per register group
-          const int n = 32 * nb + 8 * q + 4 * lhi;
-          const f32x4 bp4 = *reinterpret_cast<const f32x4*>(&sm.bp[n]);
-          const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&sm.bg[n]);
+      for (int q = 0; q < 4; ++q) {   // 4 consecutive output channels per register group
+        const int n = 32 * nb + 8 * q + 4 * lhi;
+        const f32x4 bp4 = *reinterpret_cast<const f32x4*>(&sm.bp[n]);
+        const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&sm.bg[n]);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc_p[4 * q + e] = bp4[e];
-            acc_g[4 * q + e] = bg4[e];
-          }
-        }
-      } else {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          acc_p[r] = bias_p[r];
-          acc_g[r] = bias_g[r];
+        for (int e = 0; e < 4; ++e) {
+          acc_p[4 * q + e] = bp4[e];
+          acc_g[4 * q + e] = bg4[e];
         }
       }
       int prow = 32 * mb + l32;           // pair this lane feeds as the B operand
-      // c = 256: an opaque copy per tile, so the fragment addresses derived
-      // from it are not hoisted out of the tile loop (they would hold 64
-      // registers for the whole kernel)
-      if constexpr (kWide) asm volatile("" : "+v"(prow));
+      // an opaque copy per tile, so the fragment addresses derived from it are
+      // not hoisted out of the tile loop (they would hold 64 registers for the
+      // whole kernel)
+      asm volatile("" : "+v"(prow));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        // c = 256: keep the compiler from loading every k-step's fragments
-        // ahead (128 more registers); four k-steps in flight are enough
-        if constexpr (kWide) {
-          if (ks % 4 == 0 && ks > 0) asm volatile("" ::: "memory");
-        }
+        // keep the compiler from loading every k-step's fragments ahead (128
+        // more registers); four k-steps in flight are enough
+        if (ks % 4 == 0 && ks > 0) asm volatile("" ::: "memory");
         const bf16x8 u = ld_frag(sm.y + soff<C>(prow, 2 * ks + lhi));
         const bf16x8 z = ld_frag(sm.z + soff<C>(prow, 2 * ks + lhi));
         acc_p = mfma32x32x16(wp[ks], u, acc_p);
@@ -321,24 +208,14 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
       const int id = it * K3_THREADS + tid;
       const int pr = id / (CZ / 8);
       const int cc = id - pr * (CZ / 8);
-      if constexpr (kWide) {
-        if (j0 + pr < N) {
-          u32x4 v = ld16(sm.o + pr * (C * 2) + ((cc ^ ((pr & 31) >> 1)) << 4));
-          if (pr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-          st16(p.out + (size_t(row) * N + j0 + pr) * CZ + 8 * cc, v);
-        }
-      } else {
+      if (j0 + pr < N) {
         u32x4 v = ld16(sm.o + pr * (C * 2) + ((cc ^ ((pr & 31) >> 1)) << 4));
         if (pr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        // a pair past N gets an offset past the end of out: the store is dropped
-        const int so = __builtin_amdgcn_readfirstlane((row * N + j0) * CZ * 2);
-        const uint32_t off = (j0 + pr < N) ? o_off[it] : 0x80000000u;
-        buffer_store16(rsrc_o, v, off, so);
+        st16(p.out + (size_t(row) * N + j0 + pr) * CZ + 8 * cc, v);
       }
     }
   }
 }
-
 
 // ---------------------------------------------------------------------------
 // c = 128: wave-specialised form. Waves 0-3 ("matrix waves") each own one
