@@ -12,11 +12,11 @@
 // without a transpose. n_pad is a multiple of 64 and the padded columns hold
 // +0.0, so the k loop has no tail.
 //
-// Tile: 256 x 256 outputs per block of 8 waves (2 x 4), each wave 128 (i) x
-// 64 (j) as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks. K advances 32 columns per
-// step through a 4-stage LDS ring filled by direct global->LDS loads
-// (global_load_lds_dwordx4), three steps ahead of the matrix cores, one
-// barrier per step. The ring is laid out in 256-byte lines (one line of the
+// Tile (default): 256 x 256 outputs per block of 8 waves (2 x 4), each wave
+// 128 (i) x 64 (j) as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks. K advances 64
+// columns per step through a 2-stage LDS ring filled by direct global->LDS
+// loads (global_load_lds_dwordx4), one step ahead of the matrix cores, one
+// barrier per step (other shapes: k2_config). The ring is laid out in 256-byte lines (one line of the
 // 64 four-byte banks) holding 4 rows of 32 k each, with the 16-byte chunk
 // index XOR-ed by the line index, so the 16 lanes of a fragment read hit 16
 // distinct bank groups. Rows past N are clamped to row N-1 (their results are
@@ -222,8 +222,10 @@ __global__ __launch_bounds__(K2_THREADS) void k2_contract(const K2Args p) {
     const int id = it * K2_THREADS + tid;
     const int ii = id / CPR;
     const int cc = id % CPR;
+    // y is not read again by this kernel: the non-temporal hint keeps it from
+    // displacing operand lines other tiles still read from the L2
     if (i0 + ii < N && 8 * cc < jrem)
-      st16(Y + size_t(i0 + ii) * ld + j0 + 8 * cc, ld16(smem + ii * C::YP + cc * 16));
+      __builtin_nontemporal_store(ld16(smem + ii * C::YP + cc * 16), reinterpret_cast<u32x4*>(Y + size_t(i0 + ii) * ld + j0 + 8 * cc));
   }
 }
 
