@@ -139,11 +139,11 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
   uint16_t mraw = 0;
   bool xok = false;
   auto fetch = [&](int t) {
-    const int row = t / nchunk;
+    const int row = fast_div(t, p.div_nchunk);
     const int inner = (t - row * nchunk) * K1_TP + lp;
     xok = inner < N;
     const int in_c = xok ? inner : N - 1;
-    const int bb = row / N;
+    const int bb = fast_div(row, p.div_N);
     const int fixed = row - bb * N;
     // outgoing: pair (b, fixed, inner); incoming: pair (b, inner, fixed)
     const int pi = p.incoming ? (bb * N + in_c) * N + fixed : row * N + in_c;
@@ -263,7 +263,7 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
   // lies inside its row
   // Buffer stores: a lane's byte offset inside a tile (channel row and
   // chunk) is the same for every tile and sits in a register; the tile's
-  // (row, first pair) offset is uniform and goes in the scalar offset. Every
+  // (row, first pair) offset is uniform and is added to it per store. Every
   // plane is below 2^31 bytes (the extent rule), so 32-bit offsets suffice.
   constexpr int kStoreParts = (2 * K1_GROUP * K1_TP / 8) / K1_THREADS;
   static_assert(kStoreParts == 4 && K1_THREADS / 8 * 2 == K1_GROUP, "parts 0-1: plane a, 2-3: plane b");
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
     for (int it = 0; it < kStoreParts; ++it) st_off[it] = lane_off(it);
   }
   auto store_part = [&](int t, int ob, int it) {
-    const int row = t / nchunk;
+    const int row = fast_div(t, p.div_nchunk);
     const int inner0 = (t - row * nchunk) * K1_TP;
     const int srow = (it * K1_THREADS + tid) >> 3;
     const int c16 = tid & 7;
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
       st16((it < 2 ? p.plane_a : p.plane_b) + size_t(gch) * ch_stride + size_t(row) * p.n_pad + inner0 + 8 * c16,
            v);
     } else {
-      __builtin_amdgcn_raw_buffer_store_b128(v, it < 2 ? rsrc_a : rsrc_b, st_off[it], soff, 0);
+      buffer_store16(it < 2 ? rsrc_a : rsrc_b, v, st_off[it] + uint32_t(soff));
     }
   };
   auto store = [&](int t, int ob) {

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   const size_t ch_stride = size_t(p.B) * N * p.n_pad;
 
   for (int t = blockIdx.x; t < p.ntiles; t += gridDim.x) {
-    const int row = t / p.nchunk;                      // b * N + i
+    const int row = fast_div(t, p.div_nchunk);                      // b * N + i
     const int j0 = (t - row * p.nchunk) * K3_TP;
 
     // ---- y -> pair-major LDS rows (two channels per dword) ----
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
   const int nit = (nk + 2) & ~1;
   auto tile_at = [&](int k, int& row, int& j0) {
     const int t = int(blockIdx.x) + k * G;
-    row = t / p.nchunk;                     // b * N + i
+    row = fast_div(t, p.div_nchunk);                     // b * N + i
     j0 = (t - row * p.nchunk) * K3_TP;
   };
 
@@ -333,9 +333,10 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
         const int cc = id - pr * (CZ / 8);
         u32x4 v = ld16(ob + pr * (C * 2) + ((cc ^ ((pr & 31) >> 1)) << 4));
         if (pr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        // a pair past N gets an offset past the end of out: the store is dropped
+        // a pair past N gets an offset past the end of out (0x80000000 plus a
+        // tile base below 2^31 stays below 2^32): the store is dropped
         const uint32_t off = (j0 + pr < N) ? uint32_t(id) * 16u : 0x80000000u;
-        buffer_store16(rsrc_o, v, off, so);
+        buffer_store16(rsrc_o, v, off + uint32_t(so));
       }
     };
     lds_barrier();                           // the LayerNorm waves' first tile: y rows

@@ -225,6 +225,8 @@ int run(int first_stage, int last_stage, const void* x, const void* mask, const 
       a.incoming = direction == TRIMUL_INCOMING;
       a.nchunk = (N + 63) / 64;
       a.ntiles = trimul::k1_tiles(B, N);
+      a.div_nchunk = trimul::make_fast_div(uint32_t(a.nchunk));
+      a.div_N = trimul::make_fast_div(uint32_t(N));
       a.eps = eps;
       const int groups = c / 128;
       int grid = info.cus / groups;
@@ -263,6 +265,7 @@ int run(int first_stage, int last_stage, const void* x, const void* mask, const 
       a.c = c;
       a.nchunk = (N + 63) / 64;
       a.ntiles = trimul::k3_tiles(B, N);
+      a.div_nchunk = trimul::make_fast_div(uint32_t(a.nchunk));
       a.eps = eps;
       int grid = info.cus;
       if (grid > a.ntiles) grid = a.ntiles;

@@ -41,12 +41,18 @@ __device__ __forceinline__ void unpack8(const u32x4& c, float (&v)[8]) {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// 16-byte buffer load / store at byte offset voff + soff (soff uniform)
+// 16-byte buffer load at byte offset voff + soff (soff uniform)
 __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
 }
-__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, const u32x4& v, uint32_t voff, int soff) {
-  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, soff, 0);
+// 16-byte buffer store at byte offset voff. The whole offset goes in the
+// vector operand and the scalar offset is the constant 0: a store of more
+// than 8 bytes reads its data registers over more than one cycle, and the
+// compiler only keeps the next instruction from overwriting them when the
+// scalar offset is not a register (with a register there, the first data
+// dword has been seen to take the value written by the next instruction).
+__device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, const u32x4& v, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
 }
 __device__ __forceinline__ bf16x8 ld_frag(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
 

@@ -6,6 +6,29 @@
 
 namespace trimul {
 
+// Division of an index n < 2^31 by a divisor d >= 1 fixed for a launch, as a
+// multiply-high, an add and a shift (Granlund and Montgomery, "Division by
+// invariant integers using multiplication", 1994): with l = ceil(log2 d) and
+// m = floor(2^32 (2^l - d) / d) + 1, n / d = (mulhi(n, m) + n) >> l, exact for
+// every n below 2^32 whose sum fits 32 bits (mulhi(n, m) < n < 2^31 here).
+// The kernels divide tile and row indices this way in scalar registers
+// instead of the ~35-instruction division sequence.
+struct FastDiv {
+  uint32_t m;
+  uint32_t l;
+};
+
+inline FastDiv make_fast_div(uint32_t d) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;
+  const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+  return FastDiv{uint32_t(m), l};
+}
+
+__device__ __forceinline__ int fast_div(int n, FastDiv f) {
+  return int((__umulhi(uint32_t(n), f.m) + uint32_t(n)) >> f.l);
+}
+
 // Stage 1: LayerNorm_in + gated dual projection + mask -> planes a, b.
 struct K1Args {
   const uint16_t* x;        // [B, N, N, c_z]
@@ -22,6 +45,7 @@ struct K1Args {
   int incoming;
   int nchunk;               // tiles per plane row: ceil(N / 64)
   int ntiles;               // B * N * nchunk
+  FastDiv div_nchunk, div_N;
   float eps;
 };
 
@@ -51,6 +75,7 @@ struct K3Args {
   int B, N, n_pad, c_z, c;
   int nchunk;
   int ntiles;
+  FastDiv div_nchunk;
   float eps;
 };
 
