@@ -229,6 +229,192 @@ __global__ __launch_bounds__(K2_THREADS) void k2_contract(const K2Args p) {
   }
 }
 
+// Persistent form of the default tile (256 x 256, k 64, two stages): one
+// block per CU loops over its tiles. After a tile's last k-step it sets up
+// the next tile and issues that tile's first k-step into ring stage 0, then
+// stages and stores y in two 128-row halves through the LDS past stage 0,
+// so the next tile's first operand fill is in flight during the epilogue and
+// no block is relaunched. Tiles are handed out so that the blocks of one XCD
+// work on a contiguous range of (channel, batch) matrices, as in the
+// non-persistent form. The y stores are buffer stores that are always
+// issued (rows past N at an offset past the end of the plane, dropped by the
+// hardware), so the wait for the next tile's first fill can count exactly the
+// 16 stores issued after it.
+using CfgP = K2Cfg<256, 256, 64, 2, 2, 4>;
+constexpr int K2P_YROWS = CfgP::BM / 2;                 // staged rows per half
+constexpr int K2P_STAGE_OFF = CfgP::STAGE_BYTES;        // staging starts past ring stage 0
+constexpr int K2P_SMEM = K2P_STAGE_OFF + K2P_YROWS * CfgP::YP;
+static_assert(K2P_SMEM <= 160 * 1024, "LDS");
+static_assert(CfgP::WM == 2, "one wave row per staged half");
+constexpr int K2P_STORES = 2 * (K2P_YROWS * (CfgP::BN / 8)) / K2_THREADS;   // y stores per thread per tile
+
+__global__ __launch_bounds__(K2_THREADS) void k2_contract_p(const K2Args p) {
+  using C = CfgP;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[K2P_SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int l32 = lane & 31;
+  const int lhi = lane >> 5;
+  const int wm = wave / C::WN;
+  const int wn = wave % C::WN;
+  const int N = p.N, ld = p.n_pad;
+  const int per_mat = p.tiles_m * p.tiles_n;
+  const int nb = p.nblocks;                             // tiles in all
+  const int G = gridDim.x;
+
+  // this block's tiles: logical tile first + k * step, k < count
+  int first, step, count;
+  if ((nb & 7) == 0 && (G & 7) == 0) {
+    const int per_xcd = nb >> 3, blocks_xcd = G >> 3;
+    const int x = blockIdx.x & 7, q = blockIdx.x >> 3;
+    first = x * per_xcd + q;
+    step = blocks_xcd;
+    count = q < per_xcd ? (per_xcd - q + blocks_xcd - 1) / blocks_xcd : 0;
+  } else {
+    first = blockIdx.x;
+    step = G;
+    count = first < nb ? (nb - first + G - 1) / G : 0;
+  }
+  if (count == 0) return;
+
+  const uint32_t plane_bytes = uint32_t(p.c) * uint32_t(p.B) * uint32_t(N) * uint32_t(ld) * 2u;
+  const auto rsrc_y = __builtin_amdgcn_make_buffer_rsrc(p.plane_y, 0, plane_bytes, 0x00020000);
+
+  const uint16_t* srcA[C::IA];
+  const uint16_t* srcB[C::IB];
+  int i0 = 0, j0 = 0;
+  uint32_t ybase = 0;                                   // element offset of the tile's matrix
+  auto setup = [&](int logical) {
+    const int mat = logical / per_mat;                  // = ch * B + b
+    const int tile = logical - mat * per_mat;
+    const int tm = tile / p.tiles_n;
+    const int tn = tile - tm * p.tiles_n;
+    i0 = tm * C::BM;
+    j0 = tn * C::BN;
+    const size_t base = size_t(mat) * N * ld;
+    ybase = uint32_t(base);
+    const uint16_t* Ag = p.plane_a + base;
+    const uint16_t* Bg = p.plane_b + base;
+#pragma unroll
+    for (int t = 0; t < C::IA; ++t) {
+      int r, c;
+      C::src((wave * C::IA + t) * 64 + lane, r, c);
+      srcA[t] = Ag + size_t(min(i0 + r, N - 1)) * ld + 8 * c;   // rows past N clamp to N - 1
+    }
+#pragma unroll
+    for (int t = 0; t < C::IB; ++t) {
+      int r, c;
+      C::src((wave * C::IB + t) * 64 + lane, r, c);
+      srcB[t] = Bg + size_t(min(j0 + r, N - 1)) * ld + 8 * c;
+    }
+  };
+  auto issue = [&](int kstep) {
+    uint8_t* st = smem + (kstep % C::STAGES) * C::STAGE_BYTES;
+    const int k0 = kstep * C::BK;
+#pragma unroll
+    for (int t = 0; t < C::IA; ++t)
+      load_lds16(srcA[t] + k0, st + (wave * C::IA + t) * 1024);
+#pragma unroll
+    for (int t = 0; t < C::IB; ++t)
+      load_lds16(srcB[t] + k0, st + C::A_BYTES + (wave * C::IB + t) * 1024);
+  };
+
+  constexpr int SUB = C::BK / 16;
+  int offA[C::MI][SUB], offB[C::NJ][SUB];
+#pragma unroll
+  for (int s = 0; s < SUB; ++s) {
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) offA[mi][s] = C::off(wm * C::WTM + 32 * mi + l32, 2 * s + lhi);
+#pragma unroll
+    for (int nj = 0; nj < C::NJ; ++nj) offB[nj][s] = C::A_BYTES + C::off(wn * C::WTN + 32 * nj + l32, 2 * s + lhi);
+  }
+
+  const int nk = ld / C::BK;
+  setup(first);
+  issue(0);
+  for (int k = 0; k < count; ++k) {
+    f32x16 acc[C::MI][C::NJ];
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mi][nj][r] = 0.0f;
+
+    for (int kt = 0; kt < nk; ++kt) {
+      // step kt's fill is done once only what was issued after it remains:
+      // for the first step of a later tile, the previous tile's y stores
+      if (kt == 0 && k > 0) wait_vm<K2P_STORES>();
+      else wait_vm<0>();
+      lds_barrier();
+      if (kt + 1 < nk) issue(kt + 1);
+      const uint8_t* st = smem + (kt % C::STAGES) * C::STAGE_BYTES;
+#pragma unroll
+      for (int s = 0; s < SUB; ++s) {
+        bf16x8 af[C::MI], bfr[C::NJ];
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi) af[mi] = ld_frag(st + offA[mi][s]);
+#pragma unroll
+        for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = ld_frag(st + offB[nj][s]);
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi)
+#pragma unroll
+          for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = mfma32x32x16(bfr[nj], af[mi], acc[mi][nj]);
+      }
+    }
+    lds_barrier();   // every wave is done with the ring
+
+    // the next tile's first k-step goes into ring stage 0 during the epilogue
+    const int ti0 = i0, tj0 = j0;
+    const uint32_t tybase = ybase;
+    if (k + 1 < count) {
+      setup(first + (k + 1) * step);
+      issue(0);
+    }
+
+    // ---- epilogue: y in two 128-row halves through the LDS past stage 0 ----
+    const int jrem = min(C::BN, ld - tj0);              // columns inside this row (n_pad bound)
+    constexpr int CPR = C::BN / 8;                      // 16-byte chunks per tile row
+    uint8_t* stage = smem + K2P_STAGE_OFF;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      if (wm == h) {
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi) {
+          const int ii = 32 * mi + l32;                 // row within the half
+#pragma unroll
+          for (int nj = 0; nj < C::NJ; ++nj) {
+#pragma unroll
+            for (int rg = 0; rg < 4; ++rg) {
+              const int jj = wn * C::WTN + 32 * nj + 8 * rg + 4 * lhi;
+              const u32x2 w = {pack_bf16x2(acc[mi][nj][4 * rg], acc[mi][nj][4 * rg + 1]),
+                               pack_bf16x2(acc[mi][nj][4 * rg + 2], acc[mi][nj][4 * rg + 3])};
+              *reinterpret_cast<u32x2*>(stage + ii * C::YP + jj * 2) = w;
+            }
+          }
+        }
+      }
+      lds_barrier();
+#pragma unroll
+      for (int it = 0; it < (K2P_YROWS * CPR) / K2_THREADS; ++it) {
+        const int id = it * K2_THREADS + tid;
+        const int ii = id / CPR;
+        const int cc = id % CPR;
+        const int row = ti0 + K2P_YROWS * h + ii;
+        // y is not read again here: non-temporal; a row past N or a chunk
+        // past n_pad goes past the end of the plane and is dropped
+        const uint32_t off = (row < N && 8 * cc < jrem)
+                                 ? (tybase + uint32_t(row) * uint32_t(ld) + uint32_t(tj0 + 8 * cc)) * 2u
+                                 : 0x80000000u;
+        __builtin_amdgcn_raw_buffer_store_b128(ld16(stage + ii * C::YP + cc * 16), rsrc_y, off, 0, 2);
+      }
+      lds_barrier();   // the staging rows are rewritten by the next half / the next fills
+    }
+  }
+}
+
 // explicit instantiations of every configuration's kernel (and its host stub)
 template __global__ void k2_contract<256, 256, 32, 4, 2, 4>(const K2Args);
 template __global__ void k2_contract<256, 128, 64, 3, 4, 2>(const K2Args);
@@ -245,11 +431,14 @@ using CfgTall64 = K2Cfg<128, 256, 64, 3, 2, 4>; // 128 x 256, k 64, 3 stages
 
 int g_cfg = -1;   // chosen once per process
 
+// 0: 256 x 256 k 32, 4 stages; 1: 256 x 128 k 64, 3 stages; 2 (default):
+// 256 x 256 k 64, 2 stages, persistent; 3: 128 x 256 k 64, 3 stages;
+// 4: configuration 2 without the persistent loop
 int k2_config() {
   if (g_cfg < 0) {
     int c = 2;
     if (const char* e = std::getenv("TRIMUL_K2_TILE")) c = std::atoi(e);
-    g_cfg = (c >= 0 && c <= 3) ? c : 2;
+    g_cfg = (c >= 0 && c <= 4) ? c : 2;
   }
   return g_cfg;
 }
@@ -267,7 +456,7 @@ void k2_tiles(int N, int& tiles_m, int& tiles_n) {
     case 0: tiles_of<CfgSq32>(N, tiles_m, tiles_n); break;
     case 3: tiles_of<CfgTall64>(N, tiles_m, tiles_n); break;
     case 1: tiles_of<CfgRect64>(N, tiles_m, tiles_n); break;
-    default: tiles_of<CfgSq64>(N, tiles_m, tiles_n); break;
+    default: tiles_of<CfgSq64>(N, tiles_m, tiles_n); break;   // 2 and 4
   }
 }
 
@@ -277,12 +466,19 @@ void launch_cfg(const K2Args& a, hipStream_t stream) {
                      dim3(K2_THREADS), 0, stream, a);
 }
 
-hipError_t launch_k2(const K2Args& a, hipStream_t stream) {
+hipError_t launch_k2(const K2Args& a, int max_blocks, hipStream_t stream) {
   switch (k2_config()) {
     case 0: launch_cfg<CfgSq32>(a, stream); break;
     case 3: launch_cfg<CfgTall64>(a, stream); break;
     case 1: launch_cfg<CfgRect64>(a, stream); break;
-    default: launch_cfg<CfgSq64>(a, stream); break;
+    case 4: launch_cfg<CfgSq64>(a, stream); break;
+    default: {
+      // one persistent block per CU, a multiple of 8 (one share per XCD) when possible
+      int grid = a.nblocks < max_blocks ? a.nblocks : max_blocks;
+      if (grid > 8) grid &= ~7;
+      hipLaunchKernelGGL(k2_contract_p, dim3(grid), dim3(K2_THREADS), 0, stream, a);
+      break;
+    }
   }
   return hipGetLastError();
 }

@@ -244,7 +244,7 @@ int run(int first_stage, int last_stage, const void* x, const void* mask, const 
       a.c = c;
       trimul::k2_tiles(N, a.tiles_m, a.tiles_n);
       a.nblocks = a.tiles_m * a.tiles_n * c * B;
-      e = trimul::launch_k2(a, s);
+      e = trimul::launch_k2(a, info.cus, s);
     } else {
       trimul::K3Args a;
       a.plane_y = plane_y;

@@ -80,7 +80,7 @@ struct K3Args {
 };
 
 hipError_t launch_k1(const K1Args& a, int grid_x, hipStream_t stream);
-hipError_t launch_k2(const K2Args& a, hipStream_t stream);
+hipError_t launch_k2(const K2Args& a, int max_blocks, hipStream_t stream);
 hipError_t launch_k3(const K3Args& a, int grid_x, hipStream_t stream);
 
 int k1_tiles(int B, int N);
