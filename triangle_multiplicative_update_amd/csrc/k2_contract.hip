@@ -16,10 +16,12 @@
 // 128 (i) x 64 (j) as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks. K advances 64
 // columns per step through a 2-stage LDS ring filled by direct global->LDS
 // loads (global_load_lds_dwordx4), one step ahead of the matrix cores, one
-// barrier per step (other shapes: k2_config). The ring is laid out in 256-byte lines (one line of the
-// 64 four-byte banks) holding 4 rows of 32 k each, with the 16-byte chunk
-// index XOR-ed by the line index, so the 16 lanes of a fragment read hit 16
-// distinct bank groups. Rows past N are clamped to row N-1 (their results are
+// barrier per step. The default launch is the persistent form
+// (k2_contract_p: one block per CU looping over its tiles, the next tile's
+// first fill overlapping the epilogue; other shapes: k2_config). The ring is
+// laid out in 256-byte lines (one line of the 64 four-byte banks) holding 4
+// rows of 32 k each, with the 16-byte chunk index XOR-ed by the line index,
+// so the 16 lanes of a fragment read hit 16 distinct bank groups. Rows past N are clamped to row N-1 (their results are
 // discarded). The epilogue stages the bf16 tile in LDS and writes 512-byte
 // row segments of y. Blocks are numbered so that the tiles of one (channel,
 // batch) matrix run on one XCD and share its L2.

@@ -51,10 +51,11 @@ def kernel_sha(stage: int) -> str:
 
 def stage_of(kernel_name: str):
     """Stage (1, 2, 3) of a kernel name as rocprofv3 prints it, e.g.
-    ``void trimul::k2_contract<256, ...>(trimul::K2Args)`` or
+    ``void trimul::k2_contract<256, ...>(trimul::K2Args)``,
+    ``trimul::k2_contract_p(trimul::K2Args)`` or
     ``trimul::(anonymous namespace)::k3_epilogue_ws(trimul::K3Args)``."""
     for s, n in KERNEL_NAMES.items():
-        if re.search(r"\b" + n + r"(<|_ws\b|\()", kernel_name):
+        if re.search(r"\b" + n + r"(_ws|_p)?(<|\()", kernel_name):
             return s
     return None
 
@@ -151,6 +152,29 @@ def traffic(args) -> None:
         fh.write("\n".join(md))
 
 
+def phase_means(trace_dir: str, warmup: int, steps: int):
+    """Mean duration (us) of each stage kernel in each phase of a bench.py run.
+
+    bench.py runs ``warmup`` eager steps, ``steps`` timed eager steps (HIP
+    events between the stages), then ``warmup`` and ``steps`` launches of the
+    captured graph; every step dispatches each stage kernel once, so the
+    dispatches of a stage, in start order, split into those four phases."""
+    durs: dict[int, list] = {1: [], 2: [], 3: []}
+    for r in _csv_rows(trace_dir, "kernel_trace.csv"):
+        s = stage_of(r["Kernel_Name"])
+        if s is not None:
+            durs[s].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    bounds = {"warmup": (0, warmup), "timed": (warmup, warmup + steps),
+              "graph warmup": (warmup + steps, 2 * warmup + steps), "graph": (2 * warmup + steps, 2 * (warmup + steps))}
+    out = {}
+    for s, lst in durs.items():
+        if len(lst) != 2 * (warmup + steps):
+            raise ValueError(f"stage {s}: {len(lst)} dispatches, expected {2 * (warmup + steps)}")
+        d = [v for _, v in sorted(lst)]
+        out[s] = {ph: statistics.mean(d[a:b]) / 1e3 for ph, (a, b) in bounds.items()}
+    return out
+
+
 def trace(args) -> None:
     rows = list(_csv_rows(args.stats, "kernel_stats.csv"))
     total = sum(float(r["TotalDurationNs"]) for r in rows)
@@ -163,10 +187,22 @@ def trace(args) -> None:
         md.append(f"| `{r['Name']}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                   f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                   f"{100 * float(r['TotalDurationNs']) / total:.1f} % |")
+    rec = None
     if args.bench_json:
         with open(args.bench_json) as fh:
             line = [l for l in fh if l.startswith("{")][-1]
         rec = json.loads(line)
+    if args.phases:
+        warmup, steps = (int(v) for v in args.phases.split(","))
+        pm = phase_means(args.stats, warmup, steps)
+        md += ["", f"Mean duration per phase of the run (`run_kernel_trace.csv`, each stage's dispatches in start "
+               f"order: {warmup} warmup steps, {steps} timed eager steps, {warmup} + {steps} graph launches), in us:",
+               "", "| kernel | warmup | timed | graph warmup | graph | HIP events, timed steps |", "|---|---|---|---|---|---|"]
+        for s in (1, 2, 3):
+            ev = (rec or {}).get("per_stage_us", {}).get(KERNEL_NAMES[s])
+            md.append(f"| {KERNEL_NAMES[s]} | " + " | ".join(f"{pm[s][ph]:.1f}" for ph in
+                      ("warmup", "timed", "graph warmup", "graph")) + f" | {'' if ev is None else f'{ev:.1f}'} |")
+    if rec is not None:
         md += ["", "The same process's own HIP-event timing of the timed steps (`per_stage_us` of its JSON line):",
                "", "```", json.dumps(rec.get("per_stage_us")), "```"]
     md.append("")
@@ -186,6 +222,7 @@ def main() -> None:
         k.add_argument(a, required=True)
     k.add_argument("--bench-args", default="")
     k.add_argument("--bench-json", default=None, help="file holding the profiled run's JSON line")
+    k.add_argument("--phases", default=None, help="WARMUP,STEPS of the profiled bench.py run")
     args = ap.parse_args()
     os.makedirs(args.out, exist_ok=True)
     (traffic if args.cmd == "traffic" else trace)(args)
