@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--cpu-sample-rows", type=int, default=0,
                     help="time the oracle on this many output rows only (0 = the whole call)")
+    ap.add_argument("--cpu-min-seconds", type=float, default=10.0,
+                    help="repeat the oracle sample until this much time has passed (at most 8 runs)")
     ap.add_argument("--profile-dir", default=None,
                     help="where the HBM traffic records are read (default: profiles/)")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -59,7 +61,7 @@ def measured_traffic(stage: int, workload: str, direction: str, profile_dir: str
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(inp, wl, direction, flops_per_call, sample_rows: int):
+def cpu_baseline(inp, wl, direction, flops_per_call, sample_rows: int, min_seconds: float = 10.0):
     import numpy as np
     try:
         from threadpoolctl import threadpool_info
@@ -68,18 +70,24 @@ def cpu_baseline(inp, wl, direction, flops_per_call, sample_rows: int):
     except Exception:
         threads = 1
     import oracle
+    # the sample is run whole, again and again, until min_seconds have passed
+    runs = 0
     t0 = time.perf_counter()
+    while True:
+        if sample_rows and sample_rows < wl.N:
+            oracle.forward_block(inp, direction, list(range(sample_rows)), list(range(wl.N)))
+        else:
+            oracle.forward(inp, direction)
+        runs += 1
+        dt = time.perf_counter() - t0
+        if dt >= min_seconds or runs >= 8:
+            break
     if sample_rows and sample_rows < wl.N:
-        rows = list(range(sample_rows))
-        oracle.forward_block(inp, direction, rows, list(range(wl.N)))
-        dt = time.perf_counter() - t0
-        frac = sample_rows / wl.N
-        sample = f"oracle.forward_block over {sample_rows} of {wl.N} output rows (all columns)"
+        frac = runs * sample_rows / wl.N
+        sample = f"oracle.forward_block over {sample_rows} of {wl.N} output rows (all columns), {runs} runs"
     else:
-        oracle.forward(inp, direction)
-        dt = time.perf_counter() - t0
-        frac = 1.0
-        sample = f"oracle.forward, the whole {wl.name} {direction} call"
+        frac = float(runs)
+        sample = f"oracle.forward, the whole {wl.name} {direction} call, {runs} runs"
     del np
     return {
         "value": flops_per_call * frac / dt / 1e12,
@@ -219,7 +227,7 @@ def main():
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(inp, wl, direction, F, args.cpu_sample_rows)
+        line["cpu_baseline"] = cpu_baseline(inp, wl, direction, F, args.cpu_sample_rows, args.cpu_min_seconds)
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line), flush=True)
