@@ -220,23 +220,25 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
 // ---------------------------------------------------------------------------
 // c = 128: wave-specialised form. Waves 0-3 ("matrix waves") each own one
 // 32-channel output block for both pair halves: the p_out and g_out MFMAs, the
-// gate, the out staging and the stores. Waves 4-7 ("LayerNorm waves") load y
-// and x, transpose y to pair-major rows and run LayerNorm_out and
-// LayerNorm_in (the stage-1 lane mapping: 8 lanes per pair, so z_in is
-// bit-identical), 16 pairs per wave, writing u and z for the matrix waves.
-// Each SIMD holds one wave of each kind, so the matrix cores of one overlap
-// the vector ALU work of the other. Iteration k has two barriers:
-//   phase 1: LayerNorm waves transpose the y of tile k+1 (in registers) into
-//            the shared y rows (each load instruction read whole 128-byte
-//            lines) and write z of tile k+1 (LayerNorm_in needs only x);
-//            matrix waves run tile k's MFMAs (u/z buffer k % 2) and the
-//            first pair half's gate
-//   phase 2: LayerNorm waves write u of tile k+1 and load y and x of tile
-//            k + 3 (two register sets: a tile's loads have 1.5 iterations to
-//            land); matrix waves run the second half's gate and store tile
-//            k - 1.
-// The matrix waves never wait for the transposes: their inputs were complete
-// an iteration earlier, so their work spans both phases.
+// gate, the out staging and the stores; they also load y and transpose it to
+// pair-major LDS rows (cheap permutes and 4-byte writes). Waves 4-7
+// ("LayerNorm waves") load x and run LayerNorm_in (the stage-1 lane mapping:
+// 8 lanes per pair, so z_in is bit-identical) and LayerNorm_out, 16 pairs per
+// wave, writing z and u for the matrix waves. Each SIMD holds one wave of each
+// kind, so the matrix cores of one overlap the vector ALU work of the other.
+// Iteration k has two barriers:
+//   phase 1: matrix waves run tile k's MFMAs (u/z buffer k % 2) and the first
+//            pair half's gate, then transpose the y of tile k+1 (in registers)
+//            into the shared y rows; LayerNorm waves write z of tile k+1
+//   phase 2: matrix waves run the second half's gate, store tile k-1 and load
+//            y of tile k+3; LayerNorm waves write u of tile k+1 and load x of
+//            tile k+3 (two register sets: a tile's loads have 1.5 iterations
+//            to land).
+// Loads are issued in every iteration (clamped to the block's last tile) and
+// the stores too (past the end of out where there is nothing to store):
+// vector-memory operations retire in issue order and the compiler counts the
+// waits per loop, merging the paths into it, so every path must issue the same
+// operations, or a wait for a load would also drain the newer ones.
 constexpr int K3W_PAIRS = 16;              // pairs per LayerNorm wave
 
 struct K3WsSmem {
@@ -245,13 +247,14 @@ struct K3WsSmem {
   uint8_t z[2][K3_TP * RB];                // LayerNorm_in rows
   uint8_t o[2][K3_TP * RB];                // out staging
   uint8_t y[K3_TP * RB];                   // transposed y rows of the next tile
+  float bp[128], bg[128];                  // output biases, fp32 (the accumulators' initial values)
 };
 
 __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
   constexpr int C = 128, CZ = 128;
   constexpr int NV = C / 64;               // LayerNorm chunks per lane
   constexpr int KS = C / 16;               // MFMA k-steps
-  constexpr int NY = (C / 2) * 8 / 256;    // (channel pair, 8-pair chunk) items per LayerNorm lane
+  constexpr int NY = (C / 2) * 8 / 256;    // (channel pair, 8-pair chunk) items per matrix-wave lane
   using S = K3WsSmem;
   __shared__ __attribute__((aligned(16))) S sm;
 
@@ -268,14 +271,16 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
   const int nk = int(blockIdx.x) < p.ntiles ? (p.ntiles - int(blockIdx.x) + G - 1) / G : 0;
   if (nk == 0) return;                      // the whole block: no barrier is left unmatched
   // iterations 0 .. nk do work; both kinds of wave run an even count (one
-  // idle iteration at most), so the LayerNorm waves' loop, unrolled by two,
-  // has no path that skips half of its body and its loads
+  // idle iteration at most), so the loops, unrolled by two, have no path that
+  // skips half of a body
   const int nit = (nk + 2) & ~1;
   auto tile_at = [&](int k, int& row, int& j0) {
     const int t = int(blockIdx.x) + k * G;
     row = fast_div(t, p.div_nchunk);                     // b * N + i
     j0 = (t - row * p.nchunk) * K3_TP;
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
 
   if (wave < 4) {
     // ---- matrix wave: output channels 32 * nb .. 32 * nb + 31 ----
@@ -287,20 +292,30 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
       wp[ks] = ld_frag(p.p_out + size_t(nrow) * C + 16 * ks + 8 * lhi);
       wg[ks] = ld_frag(p.g_out + size_t(nrow) * CZ + 16 * ks + 8 * lhi);
     }
-    // accumulator register r holds output channel 32*nb + 8*(r/4) + 4*lhi + r%4
-    f32x16 bias_p, bias_g;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int n = 32 * nb + 8 * (r >> 2) + 4 * lhi + (r & 3);
-      bias_p[r] = p.p_out_b ? bf16_to_f32(p.p_out_b[n]) : 0.0f;
-      bias_g[r] = p.g_out_b ? bf16_to_f32(p.g_out_b[n]) : 0.0f;
+    // the output biases go to LDS (read after the prologue's barriers):
+    // thread t stages channel t % 128 of p_out_b (t < 128) or g_out_b
+    {
+      const uint16_t* bsrc = tid < 128 ? p.p_out_b : p.g_out_b;
+      (tid < 128 ? sm.bp : sm.bg)[tid & 127] = bsrc ? bf16_to_f32(bsrc[tid & 127]) : 0.0f;
     }
+    // accumulator register r holds output channel 32*nb + 8*(r/4) + 4*lhi + r%4:
+    // its initial value, the bias, is 4 x 16 bytes of the staged biases
+    auto bias_init = [&](const float* bb) {
+      f32x16 a;
+#pragma unroll
+      for (int rg = 0; rg < 4; ++rg) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(bb + 32 * nb + 8 * rg + 4 * lhi);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a[4 * rg + q] = v[q];
+      }
+      return a;
+    };
     const auto rsrc_o = __builtin_amdgcn_make_buffer_rsrc(p.out, 0, xo_bytes, 0x00020000);
     constexpr int NST = (K3_TP * CZ / 8) / 256;   // 16-byte out chunks per matrix-wave lane
     auto mma = [&](int b, int mb, f32x16& acc_p, f32x16& acc_g) {
       const int prow = 32 * mb + l32;       // pair this lane feeds as the B operand
-      acc_p = bias_p;
-      acc_g = bias_g;
+      acc_p = bias_init(sm.bp);
+      acc_g = bias_init(sm.bg);
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 u = ld_frag(sm.u[b] + soff<C>(prow, 2 * ks + lhi));
@@ -320,10 +335,12 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
         *reinterpret_cast<u32x2*>(sm.o[b] + ooff<C>(prow, 2 * (4 * nb + rg) + lhi)) = packed;
       }
     };
+    // pair-major stores of tile k from out buffer k % 2; for k outside the
+    // block's tiles every store goes past the end of out and is dropped
     auto store = [&](int k) {
-      // ---- pair-major stores of tile k from out buffer k % 2 ----
+      const bool valid = k >= 0 && k < nk;
       int row, j0;
-      tile_at(k, row, j0);
+      tile_at(valid ? k : 0, row, j0);
       const int so = __builtin_amdgcn_readfirstlane((row * N + j0) * CZ * 2);
       const uint8_t* ob = sm.o[k & 1];
 #pragma unroll
@@ -335,79 +352,32 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
         if (pr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
         // a pair past N gets an offset past the end of out (0x80000000 plus a
         // tile base below 2^31 stays below 2^32): the store is dropped
-        const uint32_t off = (j0 + pr < N) ? uint32_t(id) * 16u : 0x80000000u;
+        const uint32_t off = (valid && j0 + pr < N) ? uint32_t(id) * 16u : 0x80000000u;
         buffer_store16(rsrc_o, v, off + uint32_t(so));
       }
     };
-    lds_barrier();                           // the LayerNorm waves' first tile: y rows
-    lds_barrier();                           // ... and u, z
-    for (int k = 0; k < nit; ++k) {
-      const int b = k & 1;
-      f32x16 p0, g0, p1, g1;
-      if (k < nk) {
-        // the second half's MFMAs overlap the first half's gate
-        mma(b, 0, p0, g0);
-        mma(b, 1, p1, g1);
-        gate(b, 0, p0, g0);
-      }
-      lds_barrier();
-      if (k < nk) gate(b, 1, p1, g1);
-      if (k >= 1 && k <= nk) store(k - 1);
-      lds_barrier();
-    }
-  } else {
-    // ---- LayerNorm wave lw: transposes its share of y, normalises pairs 16 lw .. 16 lw + 15 ----
-    const int lw = wave - 4;
-    const int ltid = tid - 256;
-    const int sub = lane & 7;                // sub-lane of a pair (stage-1 mapping)
-    const int pl = lane >> 3;                // pair within a pass of 8
-    u32x4 inw[NV], inb[NV], outw[NV], outb[NV];
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      inw[v] = ld16(p.ln_in_w + 8 * sub + 64 * v);
-      inb[v] = ld16(p.ln_in_b + 8 * sub + 64 * v);
-      outw[v] = ld16(p.ln_out_w + 8 * sub + 64 * v);
-      outb[v] = ld16(p.ln_out_b + 8 * sub + 64 * v);
-    }
     const auto rsrc_y = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.plane_y), 0,
                                                           uint32_t(ch_stride) * uint32_t(C) * 2u, 0x00020000);
-    const auto rsrc_x = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x), 0, xo_bytes, 0x00020000);
     // y item it: channel pair cp = id / 8 (channels 2 cp, 2 cp + 1), 8-pair
     // chunk jc = id % 8 (8 lanes read one channel's 128 bytes)
     uint32_t y_off[NY];
 #pragma unroll
     for (int it = 0; it < NY; ++it) {
-      const int id = it * 256 + ltid;
+      const int id = it * 256 + tid;
       y_off[it] = (2u * uint32_t(id >> 3) * uint32_t(ch_stride) + 8u * uint32_t(id & 7)) * 2u;
     }
-    // x: pass q, pair 16 lw + 8 q + pl, sub-lane sub
-    const uint32_t x_off = (uint32_t(K3W_PAIRS * lw + pl) * CZ + 8u * uint32_t(sub)) * 2u;
     const int ych = int(ch_stride) * 2;      // bytes from channel 2 cp to 2 cp + 1
-    u32x4 yas[2][NY], ybs[2][NY], xrs[2][2][NV];   // two register sets
-    // Loads are unconditional (a tile past the block's last loads the last
-    // one again): a conditional load would leave the compiler merging two
-    // versions of the registers with copies, and each copy of a register
-    // still being loaded waits for every load in flight.
-    auto prefetch = [&](int k, auto set) {
+    u32x4 yas[2][NY], ybs[2][NY];            // two register sets: y of tiles of either parity
+    auto prefetch_y = [&](int k, auto set) {
       constexpr int e = decltype(set)::value;
-      auto& ya = yas[e];
-      auto& yb = ybs[e];
-      auto& xr = xrs[e];
       int row, j0;
       tile_at(min(k, nk - 1), row, j0);
       const int sy = __builtin_amdgcn_readfirstlane((row * p.n_pad + j0) * 2);
-      const int sx = __builtin_amdgcn_readfirstlane((row * N + j0) * CZ * 2);
 #pragma unroll
       for (int it = 0; it < NY; ++it) {
-        ya[it] = buffer_load16(rsrc_y, y_off[it], sy);
-        yb[it] = buffer_load16(rsrc_y, y_off[it], sy + ych);
+        yas[e][it] = buffer_load16(rsrc_y, y_off[it], sy);
+        ybs[e][it] = buffer_load16(rsrc_y, y_off[it], sy + ych);
       }
-      // pairs past N read the next row's x (or zeros past the end); their
-      // outputs are never stored
-#pragma unroll
-      for (int q = 0; q < 2; ++q)
-#pragma unroll
-        for (int v = 0; v < NV; ++v) xr[q][v] = buffer_load16(rsrc_x, x_off + 2048u * q + 128u * v, sx);
     };
     auto transpose = [&](auto set) {
       constexpr int e = decltype(set)::value;
@@ -415,7 +385,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
       const auto& yb = ybs[e];
 #pragma unroll
       for (int it = 0; it < NY; ++it) {
-        const int id = it * 256 + ltid;
+        const int id = it * 256 + tid;
         const int cp = id >> 3;
         const int jc = id & 7;
 #pragma unroll
@@ -428,14 +398,75 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
         }
       }
     };
+    // prologue: the y rows of tile 0, with y of tiles 1 and 2 in flight in
+    // the order the loop issues them: a tile's y, one iteration's stores
+    // (past the end of out here), the next tile's y (into the set tile 0's
+    // transpose has just read)
+    prefetch_y(0, I0{});
+    prefetch_y(1, I1{});
+    store(-2);
+    transpose(I0{});
+    prefetch_y(2, I0{});
+    lds_barrier();                           // y rows of tile 0 (the LayerNorm waves: z of tile 0)
+    lds_barrier();                           // u of tile 0
+    // iteration k: tile k's matrix work; the y of tile k + 1 (set (k + 1) % 2)
+    // transposed, then refilled with tile k + 3
+    auto iteration = [&](int k, auto set) {
+      const int b = k & 1;
+      f32x16 p0, g0, p1, g1;
+      if (k < nk) {
+        // the second half's MFMAs overlap the first half's gate
+        mma(b, 0, p0, g0);
+        mma(b, 1, p1, g1);
+        gate(b, 0, p0, g0);
+      }
+      if (k + 1 < nk) transpose(set);
+      lds_barrier();
+      if (k < nk) gate(b, 1, p1, g1);
+      store(k - 1);
+      prefetch_y(k + 3, set);
+      lds_barrier();
+    };
+    for (int k = 0; k < nit; k += 2) {
+      iteration(k, I1{});
+      iteration(k + 1, I0{});
+    }
+  } else {
+    // ---- LayerNorm wave lw: normalises pairs 16 lw .. 16 lw + 15 ----
+    const int lw = wave - 4;
+    const int sub = lane & 7;                // sub-lane of a pair (stage-1 mapping)
+    const int pl = lane >> 3;                // pair within a pass of 8
+    u32x4 inw[NV], inb[NV], outw[NV], outb[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      inw[v] = ld16(p.ln_in_w + 8 * sub + 64 * v);
+      inb[v] = ld16(p.ln_in_b + 8 * sub + 64 * v);
+      outw[v] = ld16(p.ln_out_w + 8 * sub + 64 * v);
+      outb[v] = ld16(p.ln_out_b + 8 * sub + 64 * v);
+    }
+    const auto rsrc_x = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.x), 0, xo_bytes, 0x00020000);
+    // x: pass q, pair 16 lw + 8 q + pl, sub-lane sub
+    const uint32_t x_off = (uint32_t(K3W_PAIRS * lw + pl) * CZ + 8u * uint32_t(sub)) * 2u;
+    u32x4 xrs[2][2][NV];                     // two register sets
+    // pairs past N read the next row's x (or zeros past the end); their
+    // outputs are never stored
+    auto prefetch_x = [&](int k, auto set) {
+      constexpr int e = decltype(set)::value;
+      int row, j0;
+      tile_at(min(k, nk - 1), row, j0);
+      const int sx = __builtin_amdgcn_readfirstlane((row * N + j0) * CZ * 2);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int v = 0; v < NV; ++v) xrs[e][q][v] = buffer_load16(rsrc_x, x_off + 2048u * q + 128u * v, sx);
+    };
     auto ln_in = [&](int b, auto set) {
       constexpr int e = decltype(set)::value;
-      const auto& xr = xrs[e];
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const int P = K3W_PAIRS * lw + 8 * q + pl;   // pair within the tile
         u32x4 z[NV];
-        layer_norm_row<NV>(xr[q], inw, inb, p.eps, z);
+        layer_norm_row<NV>(xrs[e][q], inw, inb, p.eps, z);
 #pragma unroll
         for (int v = 0; v < NV; ++v) st16(sm.z[b] + soff<C>(P, sub + 8 * v), z[v]);
       }
@@ -452,27 +483,21 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
         for (int v = 0; v < NV; ++v) st16(sm.u[b] + soff<C>(P, sub + 8 * v), u[v]);
       }
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    // tile k lives in register set k % 2
-    prefetch(0, I0{});
-    prefetch(1, I1{});
-    transpose(I0{});
+    // tile k's x lives in register set k % 2
+    prefetch_x(0, I0{});
+    prefetch_x(1, I1{});
     ln_in(0, I0{});
-    lds_barrier();
+    prefetch_x(2, I0{});
+    lds_barrier();                           // z of tile 0; y rows of tile 0
     ln_out(0);
-    prefetch(2, I0{});
-    lds_barrier();
+    lds_barrier();                           // u of tile 0
     // iteration k works on tile k + 1 (set (k + 1) % 2) and refills that set
     // with tile k + 3
     auto iteration = [&](int k, auto set) {
-      if (k + 1 < nk) {
-        transpose(set);
-        ln_in((k + 1) & 1, set);
-      }
+      if (k + 1 < nk) ln_in((k + 1) & 1, set);
       lds_barrier();
       if (k + 1 < nk) ln_out((k + 1) & 1);
-      prefetch(k + 3, set);
+      prefetch_x(k + 3, set);
       lds_barrier();
     };
     for (int k = 0; k < nit; k += 2) {
