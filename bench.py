@@ -103,7 +103,7 @@ def cpu_baseline(inp, wl, direction, flops_per_call, sample_rows: int, min_secon
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "the library runs on one GPU per process; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)
         sys.exit(2)
 
