@@ -48,6 +48,9 @@ CASES = [
     (2, 136, 256, "bernoulli", True),
     (1, 45, 256, "padded", False),
     (3, 24, 128, "none", True),
+    # several stage-2 tiles per persistent block, the last one ragged
+    (1, 300, 128, "padded", True),
+    (1, 520, 128, "bernoulli", True),
 ]
 
 
