@@ -431,18 +431,18 @@ using CfgRect64 = K2Cfg<256, 128, 64, 3, 4, 2>; // 256 x 128, k 64, 3 stages
 using CfgSq64 = K2Cfg<256, 256, 64, 2, 2, 4>;   // 256 x 256, k 64, 2 stages
 using CfgTall64 = K2Cfg<128, 256, 64, 3, 2, 4>; // 128 x 256, k 64, 3 stages
 
-int g_cfg = -1;   // chosen once per process
-
 // 0: 256 x 256 k 32, 4 stages; 1: 256 x 128 k 64, 3 stages; 2 (default):
 // 256 x 256 k 64, 2 stages, persistent; 3: 128 x 256 k 64, 3 stages;
 // 4: configuration 2 without the persistent loop
 int k2_config() {
-  if (g_cfg < 0) {
+  // read once per process (a function-local static: initialised exactly once
+  // even when several host threads make the first call together)
+  static const int cfg = [] {
     int c = 2;
     if (const char* e = std::getenv("TRIMUL_K2_TILE")) c = std::atoi(e);
-    g_cfg = (c >= 0 && c <= 4) ? c : 2;
-  }
-  return g_cfg;
+    return (c >= 0 && c <= 4) ? c : 2;
+  }();
+  return cfg;
 }
 
 template <class C>
