@@ -247,6 +247,7 @@ constexpr int K2P_YROWS = CfgP::BM / 2;                 // staged rows per half
 constexpr int K2P_STAGE_OFF = CfgP::STAGE_BYTES;        // staging starts past ring stage 0
 constexpr int K2P_SMEM = K2P_STAGE_OFF + K2P_YROWS * CfgP::YP;
 static_assert(K2P_SMEM <= 160 * 1024, "LDS");
+static_assert(K2P_SMEM >= CfgP::RING_BYTES, "the LDS array holds both ring stages");
 static_assert(CfgP::WM == 2, "one wave row per staged half");
 constexpr int K2P_STORES = 2 * (K2P_YROWS * (CfgP::BN / 8)) / K2_THREADS;   // y stores per thread per tile
 
