@@ -460,27 +460,31 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
 #pragma unroll
         for (int v = 0; v < NV; ++v) xrs[e][q][v] = buffer_load16(rsrc_x, x_off + 2048u * q + 128u * v, sx);
     };
+    // both passes (pairs 16 lw + pl and 16 lw + 8 + pl) in one interleaved
+    // LayerNorm: the same bits per pair as layer_norm_row (z_in as stage 1's)
+    const int P0 = K3W_PAIRS * lw + pl, P1 = P0 + 8;   // pairs within the tile
     auto ln_in = [&](int b, auto set) {
       constexpr int e = decltype(set)::value;
+      u32x4 z0[NV], z1[NV];
+      layer_norm_rows2<NV>(xrs[e][0], xrs[e][1], inw, inb, p.eps, z0, z1);
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int P = K3W_PAIRS * lw + 8 * q + pl;   // pair within the tile
-        u32x4 z[NV];
-        layer_norm_row<NV>(xrs[e][q], inw, inb, p.eps, z);
-#pragma unroll
-        for (int v = 0; v < NV; ++v) st16(sm.z[b] + soff<C>(P, sub + 8 * v), z[v]);
+      for (int v = 0; v < NV; ++v) {
+        st16(sm.z[b] + soff<C>(P0, sub + 8 * v), z0[v]);
+        st16(sm.z[b] + soff<C>(P1, sub + 8 * v), z1[v]);
       }
     };
     auto ln_out = [&](int b) {
+      u32x4 y0[NV], y1[NV], u0[NV], u1[NV];
 #pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int P = K3W_PAIRS * lw + 8 * q + pl;
-        u32x4 yr[NV], u[NV];
+      for (int v = 0; v < NV; ++v) {
+        y0[v] = ld16(sm.y + soff<C>(P0, sub + 8 * v));
+        y1[v] = ld16(sm.y + soff<C>(P1, sub + 8 * v));
+      }
+      layer_norm_rows2<NV>(y0, y1, outw, outb, p.eps, u0, u1);
 #pragma unroll
-        for (int v = 0; v < NV; ++v) yr[v] = ld16(sm.y + soff<C>(P, sub + 8 * v));
-        layer_norm_row<NV>(yr, outw, outb, p.eps, u);
-#pragma unroll
-        for (int v = 0; v < NV; ++v) st16(sm.u[b] + soff<C>(P, sub + 8 * v), u[v]);
+      for (int v = 0; v < NV; ++v) {
+        st16(sm.u[b] + soff<C>(P0, sub + 8 * v), u0[v]);
+        st16(sm.u[b] + soff<C>(P1, sub + 8 * v), u1[v]);
       }
     };
     // tile k's x lives in register set k % 2

@@ -192,6 +192,85 @@ __device__ __forceinline__ void layer_norm_row_wb(const u32x4 (&xin)[NV], WB&& a
   }
 }
 
+// Two rows at once (both with the register-resident affine): every step is
+// taken for row 0 and then row 1 before the next step, so the two dependency
+// chains (the lane reductions above all) overlap where one wave per SIMD
+// would otherwise wait on each. Each row sees exactly the operations of
+// layer_norm_row in the same order, so its bits are the same.
+template <int NV>
+__device__ __forceinline__ void layer_norm_rows2(const u32x4 (&x0)[NV], const u32x4 (&x1)[NV],
+                                                 const u32x4 (&w)[NV], const u32x4 (&b)[NV], float eps,
+                                                 u32x4 (&z0)[NV], u32x4 (&z1)[NV]) {
+#pragma clang fp contract(off)
+  static_assert(NV <= 2, "both rows are kept unpacked");
+  constexpr float inv_n = 1.0f / float(64 * NV);
+  float v[2][NV][8];
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
+    unpack8(x0[c], v[0][c]);
+    unpack8(x1[c], v[1][c]);
+  }
+  float sp[2][4];
+#pragma unroll
+  for (int c = 0; c < NV; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = 8 * c + e;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) sp[r][i & 3] = (i < 4) ? v[r][c][e] : sp[r][i & 3] + v[r][c][e];
+    }
+  float s[2], mean[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) s[r] = (sp[r][0] + sp[r][1]) + (sp[r][2] + sp[r][3]);
+  // sum_lanes8 on both rows, step by step
+#pragma unroll
+  for (int r = 0; r < 2; ++r) s[r] = s[r] + dpp_f<0xB1>(s[r]);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) s[r] = s[r] + dpp_f<0x4E>(s[r]);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) s[r] = s[r] + dpp_f<0x141>(s[r]);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) mean[r] = s[r] * inv_n;
+  float ssp[2][4];
+#pragma unroll
+  for (int c = 0; c < NV; ++c)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int i = 8 * c + e;
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const float d = v[r][c][e] - mean[r];
+        ssp[r][i & 3] = (i < 4) ? d * d : __builtin_fmaf(d, d, ssp[r][i & 3]);
+      }
+    }
+  float ss[2], rstd[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) ss[r] = (ssp[r][0] + ssp[r][1]) + (ssp[r][2] + ssp[r][3]);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) ss[r] = ss[r] + dpp_f<0xB1>(ss[r]);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) ss[r] = ss[r] + dpp_f<0x4E>(ss[r]);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) ss[r] = ss[r] + dpp_f<0x141>(ss[r]);
+#pragma unroll
+  for (int r = 0; r < 2; ++r) rstd[r] = __builtin_amdgcn_rsqf(ss[r] * inv_n + eps);
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
+    float wv[8], bv[8];
+    unpack8(w[c], wv);
+    unpack8(b[c], bv);
+    float o[2][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+#pragma unroll
+      for (int r = 0; r < 2; ++r) o[r][e] = __builtin_fmaf((v[r][c][e] - mean[r]) * rstd[r], wv[e], bv[e]);
+    z0[c] = u32x4{pack_bf16x2(o[0][0], o[0][1]), pack_bf16x2(o[0][2], o[0][3]), pack_bf16x2(o[0][4], o[0][5]),
+                  pack_bf16x2(o[0][6], o[0][7])};
+    z1[c] = u32x4{pack_bf16x2(o[1][0], o[1][1]), pack_bf16x2(o[1][2], o[1][3]), pack_bf16x2(o[1][4], o[1][5]),
+                  pack_bf16x2(o[1][6], o[1][7])};
+  }
+}
+
 // affine parameters held in registers as packed bf16 (chunk c of this lane)
 template <int NV>
 __device__ __forceinline__ void layer_norm_row(const u32x4 (&xin)[NV], const u32x4 (&w)[NV],
