@@ -192,23 +192,33 @@ __device__ __forceinline__ void layer_norm_row_wb(const u32x4 (&xin)[NV], WB&& a
   }
 }
 
-// Two rows at once (both with the register-resident affine): every step is
-// taken for row 0 and then row 1 before the next step, so the two dependency
-// chains (the lane reductions above all) overlap where one wave per SIMD
-// would otherwise wait on each. Each row sees exactly the operations of
-// layer_norm_row in the same order, so its bits are the same.
-template <int NV>
-__device__ __forceinline__ void layer_norm_rows2(const u32x4 (&x0)[NV], const u32x4 (&x1)[NV],
-                                                 const u32x4 (&w)[NV], const u32x4 (&b)[NV], float eps,
-                                                 u32x4 (&z0)[NV], u32x4 (&z1)[NV]) {
+// Two rows at once, each with its own affine source: every step is taken for
+// row 0 and then row 1 before the next step, so the two dependency chains
+// (the lane reductions above all) overlap where one wave per SIMD would
+// otherwise wait on each. Each row sees exactly the operations of
+// layer_norm_row_wb in the same order, so its bits are the same (rows of 4 or
+// more chunks per lane are re-unpacked per pass, as there).
+template <int NV, class WB0, class WB1>
+__device__ __forceinline__ void layer_norm_rows2_wb(const u32x4 (&x0)[NV], const u32x4 (&x1)[NV], WB0&& affine0,
+                                                    WB1&& affine1, float eps, u32x4 (&z0)[NV],
+                                                    u32x4 (&z1)[NV]) {
 #pragma clang fp contract(off)
-  static_assert(NV <= 2, "both rows are kept unpacked");
   constexpr float inv_n = 1.0f / float(64 * NV);
-  float v[2][NV][8];
+  constexpr bool kKeep = NV <= 2;
+  float v[2][kKeep ? NV : 1][8];
+  auto elem = [&](int r, int c, int e) -> float {
+    if constexpr (kKeep) return v[r][c][e];
+    else {
+      const u32x4& xc = r == 0 ? x0[c] : x1[c];
+      return (e & 1) ? bf16_hi(xc[e >> 1]) : bf16_lo(xc[e >> 1]);
+    }
+  };
+  if constexpr (kKeep) {
 #pragma unroll
-  for (int c = 0; c < NV; ++c) {
-    unpack8(x0[c], v[0][c]);
-    unpack8(x1[c], v[1][c]);
+    for (int c = 0; c < NV; ++c) {
+      unpack8(x0[c], v[0][c]);
+      unpack8(x1[c], v[1][c]);
+    }
   }
   float sp[2][4];
 #pragma unroll
@@ -217,7 +227,7 @@ __device__ __forceinline__ void layer_norm_rows2(const u32x4 (&x0)[NV], const u3
     for (int e = 0; e < 8; ++e) {
       const int i = 8 * c + e;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) sp[r][i & 3] = (i < 4) ? v[r][c][e] : sp[r][i & 3] + v[r][c][e];
+      for (int r = 0; r < 2; ++r) sp[r][i & 3] = (i < 4) ? elem(r, c, e) : sp[r][i & 3] + elem(r, c, e);
     }
   float s[2], mean[2];
 #pragma unroll
@@ -239,7 +249,7 @@ __device__ __forceinline__ void layer_norm_rows2(const u32x4 (&x0)[NV], const u3
       const int i = 8 * c + e;
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
-        const float d = v[r][c][e] - mean[r];
+        const float d = elem(r, c, e) - mean[r];
         ssp[r][i & 3] = (i < 4) ? d * d : __builtin_fmaf(d, d, ssp[r][i & 3]);
       }
     }
@@ -256,18 +266,46 @@ __device__ __forceinline__ void layer_norm_rows2(const u32x4 (&x0)[NV], const u3
   for (int r = 0; r < 2; ++r) rstd[r] = __builtin_amdgcn_rsqf(ss[r] * inv_n + eps);
 #pragma unroll
   for (int c = 0; c < NV; ++c) {
-    float wv[8], bv[8];
-    unpack8(w[c], wv);
-    unpack8(b[c], bv);
+    float wv[2][8], bv[2][8];
+    affine0(c, wv[0], bv[0]);
+    affine1(c, wv[1], bv[1]);
     float o[2][8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
 #pragma unroll
-      for (int r = 0; r < 2; ++r) o[r][e] = __builtin_fmaf((v[r][c][e] - mean[r]) * rstd[r], wv[e], bv[e]);
+      for (int r = 0; r < 2; ++r) o[r][e] = __builtin_fmaf((elem(r, c, e) - mean[r]) * rstd[r], wv[r][e], bv[r][e]);
     z0[c] = u32x4{pack_bf16x2(o[0][0], o[0][1]), pack_bf16x2(o[0][2], o[0][3]), pack_bf16x2(o[0][4], o[0][5]),
                   pack_bf16x2(o[0][6], o[0][7])};
     z1[c] = u32x4{pack_bf16x2(o[1][0], o[1][1]), pack_bf16x2(o[1][2], o[1][3]), pack_bf16x2(o[1][4], o[1][5]),
                   pack_bf16x2(o[1][6], o[1][7])};
+  }
+}
+
+// two rows with one affine held in registers as packed bf16
+template <int NV>
+__device__ __forceinline__ void layer_norm_rows2(const u32x4 (&x0)[NV], const u32x4 (&x1)[NV],
+                                                 const u32x4 (&w)[NV], const u32x4 (&b)[NV], float eps,
+                                                 u32x4 (&z0)[NV], u32x4 (&z1)[NV]) {
+  auto aff = [&](int c, float (&wv)[8], float (&bv)[8]) {
+    unpack8(w[c], wv);
+    unpack8(b[c], bv);
+  };
+  layer_norm_rows2_wb<NV>(x0, x1, aff, aff, eps, z0, z1);
+}
+
+// fp32 affine rows in LDS (see layer_norm_row_lds): this lane's 8 + 8 values of chunk c
+__device__ __forceinline__ void lds_affine8(const float* w, const float* b, int sub, int c, float (&wv)[8],
+                                            float (&bv)[8]) {
+  const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + 8 * sub + 64 * c);
+  const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + 8 * sub + 64 * c + 4);
+  const f32x4 b0 = *reinterpret_cast<const f32x4*>(b + 8 * sub + 64 * c);
+  const f32x4 b1 = *reinterpret_cast<const f32x4*>(b + 8 * sub + 64 * c + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    wv[e] = w0[e];
+    wv[4 + e] = w1[e];
+    bv[e] = b0[e];
+    bv[4 + e] = b1[e];
   }
 }
 
@@ -287,19 +325,8 @@ __device__ __forceinline__ void layer_norm_row(const u32x4 (&xin)[NV], const u32
 template <int NV>
 __device__ __forceinline__ void layer_norm_row_lds(const u32x4 (&xin)[NV], const float* w, const float* b,
                                                    int sub, float eps, u32x4 (&zout)[NV]) {
-  layer_norm_row_wb<NV>(xin, [&](int c, float (&wv)[8], float (&bv)[8]) {
-    const f32x4 w0 = *reinterpret_cast<const f32x4*>(w + 8 * sub + 64 * c);
-    const f32x4 w1 = *reinterpret_cast<const f32x4*>(w + 8 * sub + 64 * c + 4);
-    const f32x4 b0 = *reinterpret_cast<const f32x4*>(b + 8 * sub + 64 * c);
-    const f32x4 b1 = *reinterpret_cast<const f32x4*>(b + 8 * sub + 64 * c + 4);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      wv[e] = w0[e];
-      wv[4 + e] = w1[e];
-      bv[e] = b0[e];
-      bv[4 + e] = b1[e];
-    }
-  }, eps, zout);
+  layer_norm_row_wb<NV>(xin, [&](int c, float (&wv)[8], float (&bv)[8]) { lds_affine8(w, b, sub, c, wv, bv); },
+                        eps, zout);
 }
 
 // Widen a bf16 vector of length n into an fp32 LDS array (block-cooperative;
