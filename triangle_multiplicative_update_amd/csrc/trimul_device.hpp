@@ -192,92 +192,84 @@ __device__ __forceinline__ void layer_norm_row_wb(const u32x4 (&xin)[NV], WB&& a
   }
 }
 
-// Two rows at once, each with its own affine source: every step is taken for
-// row 0 and then row 1 before the next step, so the two dependency chains
-// (the lane reductions above all) overlap where one wave per SIMD would
-// otherwise wait on each. Each row sees exactly the operations of
+// R rows at once: every step is taken for each row before the next step, so
+// the rows' dependency chains (the lane reductions above all) overlap where
+// one wave per SIMD would otherwise wait on each. affine(r, c, wv, bv) gives
+// row r's affine for chunk c. Each row sees exactly the operations of
 // layer_norm_row_wb in the same order, so its bits are the same (rows of 4 or
 // more chunks per lane are re-unpacked per pass, as there).
-template <int NV, class WB0, class WB1>
-__device__ __forceinline__ void layer_norm_rows2_wb(const u32x4 (&x0)[NV], const u32x4 (&x1)[NV], WB0&& affine0,
-                                                    WB1&& affine1, float eps, u32x4 (&z0)[NV],
-                                                    u32x4 (&z1)[NV]) {
+template <int NV, int R, class WB>
+__device__ __forceinline__ void layer_norm_rows_wb(const u32x4 (&x)[R][NV], WB&& affine, float eps,
+                                                   u32x4 (&z)[R][NV]) {
 #pragma clang fp contract(off)
   constexpr float inv_n = 1.0f / float(64 * NV);
   constexpr bool kKeep = NV <= 2;
-  float v[2][kKeep ? NV : 1][8];
+  float v[R][kKeep ? NV : 1][8];
   auto elem = [&](int r, int c, int e) -> float {
     if constexpr (kKeep) return v[r][c][e];
-    else {
-      const u32x4& xc = r == 0 ? x0[c] : x1[c];
-      return (e & 1) ? bf16_hi(xc[e >> 1]) : bf16_lo(xc[e >> 1]);
-    }
+    else return (e & 1) ? bf16_hi(x[r][c][e >> 1]) : bf16_lo(x[r][c][e >> 1]);
   };
   if constexpr (kKeep) {
 #pragma unroll
-    for (int c = 0; c < NV; ++c) {
-      unpack8(x0[c], v[0][c]);
-      unpack8(x1[c], v[1][c]);
-    }
+    for (int c = 0; c < NV; ++c)
+#pragma unroll
+      for (int r = 0; r < R; ++r) unpack8(x[r][c], v[r][c]);
   }
-  float sp[2][4];
+  float sp[R][4];
 #pragma unroll
   for (int c = 0; c < NV; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int i = 8 * c + e;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) sp[r][i & 3] = (i < 4) ? elem(r, c, e) : sp[r][i & 3] + elem(r, c, e);
+      for (int r = 0; r < R; ++r) sp[r][i & 3] = (i < 4) ? elem(r, c, e) : sp[r][i & 3] + elem(r, c, e);
     }
-  float s[2], mean[2];
+  float s[R], mean[R];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) s[r] = (sp[r][0] + sp[r][1]) + (sp[r][2] + sp[r][3]);
-  // sum_lanes8 on both rows, step by step
+  for (int r = 0; r < R; ++r) s[r] = (sp[r][0] + sp[r][1]) + (sp[r][2] + sp[r][3]);
+  // sum_lanes8 on every row, step by step
 #pragma unroll
-  for (int r = 0; r < 2; ++r) s[r] = s[r] + dpp_f<0xB1>(s[r]);
+  for (int r = 0; r < R; ++r) s[r] = s[r] + dpp_f<0xB1>(s[r]);
 #pragma unroll
-  for (int r = 0; r < 2; ++r) s[r] = s[r] + dpp_f<0x4E>(s[r]);
+  for (int r = 0; r < R; ++r) s[r] = s[r] + dpp_f<0x4E>(s[r]);
 #pragma unroll
-  for (int r = 0; r < 2; ++r) s[r] = s[r] + dpp_f<0x141>(s[r]);
+  for (int r = 0; r < R; ++r) s[r] = s[r] + dpp_f<0x141>(s[r]);
 #pragma unroll
-  for (int r = 0; r < 2; ++r) mean[r] = s[r] * inv_n;
-  float ssp[2][4];
+  for (int r = 0; r < R; ++r) mean[r] = s[r] * inv_n;
+  float ssp[R][4];
 #pragma unroll
   for (int c = 0; c < NV; ++c)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int i = 8 * c + e;
 #pragma unroll
-      for (int r = 0; r < 2; ++r) {
+      for (int r = 0; r < R; ++r) {
         const float d = elem(r, c, e) - mean[r];
         ssp[r][i & 3] = (i < 4) ? d * d : __builtin_fmaf(d, d, ssp[r][i & 3]);
       }
     }
-  float ss[2], rstd[2];
+  float ss[R], rstd[R];
 #pragma unroll
-  for (int r = 0; r < 2; ++r) ss[r] = (ssp[r][0] + ssp[r][1]) + (ssp[r][2] + ssp[r][3]);
+  for (int r = 0; r < R; ++r) ss[r] = (ssp[r][0] + ssp[r][1]) + (ssp[r][2] + ssp[r][3]);
 #pragma unroll
-  for (int r = 0; r < 2; ++r) ss[r] = ss[r] + dpp_f<0xB1>(ss[r]);
+  for (int r = 0; r < R; ++r) ss[r] = ss[r] + dpp_f<0xB1>(ss[r]);
 #pragma unroll
-  for (int r = 0; r < 2; ++r) ss[r] = ss[r] + dpp_f<0x4E>(ss[r]);
+  for (int r = 0; r < R; ++r) ss[r] = ss[r] + dpp_f<0x4E>(ss[r]);
 #pragma unroll
-  for (int r = 0; r < 2; ++r) ss[r] = ss[r] + dpp_f<0x141>(ss[r]);
+  for (int r = 0; r < R; ++r) ss[r] = ss[r] + dpp_f<0x141>(ss[r]);
 #pragma unroll
-  for (int r = 0; r < 2; ++r) rstd[r] = __builtin_amdgcn_rsqf(ss[r] * inv_n + eps);
+  for (int r = 0; r < R; ++r) rstd[r] = __builtin_amdgcn_rsqf(ss[r] * inv_n + eps);
 #pragma unroll
   for (int c = 0; c < NV; ++c) {
-    float wv[2][8], bv[2][8];
-    affine0(c, wv[0], bv[0]);
-    affine1(c, wv[1], bv[1]);
-    float o[2][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
+    for (int r = 0; r < R; ++r) {
+      float wv[8], bv[8], o[8];
+      affine(r, c, wv, bv);
 #pragma unroll
-      for (int r = 0; r < 2; ++r) o[r][e] = __builtin_fmaf((elem(r, c, e) - mean[r]) * rstd[r], wv[r][e], bv[r][e]);
-    z0[c] = u32x4{pack_bf16x2(o[0][0], o[0][1]), pack_bf16x2(o[0][2], o[0][3]), pack_bf16x2(o[0][4], o[0][5]),
-                  pack_bf16x2(o[0][6], o[0][7])};
-    z1[c] = u32x4{pack_bf16x2(o[1][0], o[1][1]), pack_bf16x2(o[1][2], o[1][3]), pack_bf16x2(o[1][4], o[1][5]),
-                  pack_bf16x2(o[1][6], o[1][7])};
+      for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf((elem(r, c, e) - mean[r]) * rstd[r], wv[e], bv[e]);
+      z[r][c] = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                      pack_bf16x2(o[6], o[7])};
+    }
   }
 }
 
@@ -286,11 +278,21 @@ template <int NV>
 __device__ __forceinline__ void layer_norm_rows2(const u32x4 (&x0)[NV], const u32x4 (&x1)[NV],
                                                  const u32x4 (&w)[NV], const u32x4 (&b)[NV], float eps,
                                                  u32x4 (&z0)[NV], u32x4 (&z1)[NV]) {
-  auto aff = [&](int c, float (&wv)[8], float (&bv)[8]) {
+  u32x4 x[2][NV], z[2][NV];
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
+    x[0][c] = x0[c];
+    x[1][c] = x1[c];
+  }
+  layer_norm_rows_wb<NV, 2>(x, [&](int, int c, float (&wv)[8], float (&bv)[8]) {
     unpack8(w[c], wv);
     unpack8(b[c], bv);
-  };
-  layer_norm_rows2_wb<NV>(x0, x1, aff, aff, eps, z0, z1);
+  }, eps, z);
+#pragma unroll
+  for (int c = 0; c < NV; ++c) {
+    z0[c] = z[0][c];
+    z1[c] = z[1][c];
+  }
 }
 
 // fp32 affine rows in LDS (see layer_norm_row_lds): this lane's 8 + 8 values of chunk c
