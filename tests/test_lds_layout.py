@@ -9,8 +9,8 @@ per extra distinct address on the busiest bank.
 
 Each address function below restates, in Python, the index arithmetic of the
 C++ function or expression it names, so that a change to a layout there has
-to be mirrored here and re-checked. The stage-2 ring and the stage-3 tiles are
-conflict-free; stage 1's padded z and staging tiles cost 384 extra cycles per
+to be mirrored here and re-checked. The stage-2 ring and the stage-3 tiles
+(including the c = 256 form's direct-load staging) are conflict-free; stage 1's padded z and staging tiles cost 384 extra cycles per
 tile, the count SQ_LDS_BANK_CONFLICT reads for that kernel (13.8 K per CU over
 36 tiles at N = 768).
 """
@@ -106,6 +106,46 @@ def test_stage3_tiles_are_conflict_free(C):
                         cp, jc = i >> 3, i & 7
                         addr.append(soff(8 * jc + 2 * q + odd, cp >> 2, C) + 4 * (cp & 3))
                     assert extra_cycles(addr, 4) == 0
+
+
+# ---- stage 3 at c = 256: the direct-load staging of the next tile ----
+def ys_row(ch):
+    """staging row of channel ch (row r holds channel r ^ ((r >> 1) & 1), an involution)"""
+    return ch ^ ((ch >> 1) & 1)
+
+
+def test_stage3_wide_staging_is_conflict_free_and_complete():
+    # the direct loads: slot s = 64 * (4 * wave + q) + lane of the y staging holds
+    # channel ys_row(s >> 3), pair chunk s & 7 -- every (channel, chunk) exactly once
+    seen = set()
+    for s in range(256 * 8):
+        r, jc = s >> 3, s & 7
+        seen.add((ys_row(r), jc))
+        assert ys_row(ys_row(r)) == r
+    assert len(seen) == 256 * 8
+    # the transpose reads (16 bytes): item id = it * 512 + t, channel pair cp = id >> 3,
+    # chunk jc = id & 7, channels 2 cp and 2 cp + 1 from their staging rows
+    for it in range(2):
+        for w0 in range(0, 512, 64):
+            for odd in (0, 1):
+                addr = []
+                for l in range(64):
+                    i = it * 512 + w0 + l
+                    addr.append(ys_row(2 * (i >> 3) + odd) * 128 + (i & 7) * 16)
+                assert extra_cycles(addr, 16) == 0
+    # x in the z tile: chunk c of pair lp at position c ^ 8 (lp & 1); LayerNorm_in
+    # lane (lp = t >> 3, sub = t & 7) reads chunks sub + 8 v
+    for w0 in range(0, 512, 64):
+        for v in range(4):
+            addr = []
+            for l in range(64):
+                t = w0 + l
+                lp, sub = t >> 3, t & 7
+                addr.append(lp * 512 + (((sub + 8 * v) ^ ((lp & 1) << 3)) << 4))
+            assert extra_cycles(addr, 16) == 0
+    # the same reads without the permutations would conflict
+    plain = [((2 * (l >> 3)) * 128 + (l & 7) * 16) for l in range(64)]
+    assert extra_cycles(plain, 16) > 0
 
 
 # ---- stage 3's out staging: ooff<C> (8-byte unit u of row r at unit u ^ (r % 32)) ----

@@ -37,21 +37,7 @@ namespace {
 
 constexpr int K2_THREADS = 512;
 
-typedef __attribute__((address_space(3))) void lds_void;
-
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
-
-// one 16-byte-per-lane global -> LDS copy: lane l's 16 bytes land at lds + 16 l
-__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
-}
-
-// wait until at most n vector-memory operations of this wave are outstanding
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
-}
 
 // Block tile BM (i) x BN (j), k step BK, STAGES-deep ring, 8 waves as WM x WN.
 template <int BM_, int BN_, int BK_, int STAGES_, int WM_, int WN_>

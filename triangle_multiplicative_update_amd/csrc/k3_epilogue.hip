@@ -36,8 +36,9 @@ template <int C>
 struct K3Smem {
   static constexpr int RB = C * 2;         // row bytes (pair-major, no padding)
   uint8_t y[K3_TP * RB];                   // y, then u
-  uint8_t z[K3_TP * RB];                   // z_in
+  uint8_t z[K3_TP * RB];                   // x of the tile (direct loads), then z_in in place
   uint8_t o[K3_TP * RB];                   // out staging
+  uint8_t ys[C * K3_TP * 2];               // y of the next tile, channel-major (direct loads)
   float inw[C], inb[C], outw[C], outb[C], bp[C], bg[C];   // LayerNorm affines, output biases
 };
 
@@ -56,14 +57,23 @@ __device__ __forceinline__ int ooff(int r, int unit) {
   return r * (C * 2) + ((unit ^ (r & 31)) << 3);
 }
 
-// c = 256 form. Every wave runs every phase of a tile: y is loaded and
-// transposed to pair-major LDS rows two channels per dword, x is loaded and
-// LayerNorm_in (stage-1 lane mapping) writes z, LayerNorm_out runs in place on
-// the y rows, then each wave computes two (32-channel block, pair half) jobs
-// of the output projection and gate, and the tile is stored pair-major. The
-// 32 output channels' weights of a wave take 128 registers, so the LayerNorm
-// affines and the output biases live in LDS as fp32 and nothing is prefetched
-// a tile ahead.
+// c = 256 form. Every wave runs every phase of a tile. The 32 output
+// channels' weights of a wave take 128 registers, so nothing is prefetched
+// into registers: the next tile's y and x travel by direct global -> LDS
+// loads while this tile is processed, y into a channel-major staging tile
+// (issued once this tile's y has been transposed out of it), x into the z
+// tile (issued once this tile's MFMAs have read z). Per tile:
+//   wait for y(t), x(t); barrier
+//   y staging -> pair-major y rows (two channels per dword); LayerNorm_in
+//   in place on the x rows of the z tile (stage-1 lane mapping); barrier
+//   issue y(t+1); LayerNorm_out in place on the y rows; barrier
+//   two (32-channel block, pair half) jobs per wave of the output projection
+//   and gate into the out staging; barrier
+//   issue x(t+1); pair-major stores of tile t
+// Every store is issued (a pair past N at an offset past the end of out,
+// dropped by the hardware), so the wait at the top of a tile is exact: only
+// the previous tile's stores may still be in flight. The LayerNorm affines
+// and output biases live in LDS as fp32.
 template <int C>
 __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   static_assert(C == 256, "the c = 128 form is k3_epilogue_ws");
@@ -74,14 +84,26 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   constexpr int JOBS = 2 * NB / 8;         // (channel block, pair half) jobs per wave
   constexpr int NY = (C / 2) * 8 / K3_THREADS;   // (channel pair, 8-pair chunk) items per thread
   constexpr int NST = (K3_TP * CZ / 8) / K3_THREADS;   // 16-byte out chunks per thread per tile
+  constexpr int NLD = K3_TP * C * 2 / 1024 / 8;        // 1 KB direct loads per wave per tile and tensor
+  static_assert(NLD == 4 && NST == 4, "wait counts below assume 4 loads and 4 stores per wave");
   using S = K3Smem<C>;
   __shared__ __attribute__((aligned(16))) S sm;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int lhi = lane >> 5;
+
+  const int N = p.N;
+  const int G = gridDim.x;
+  const int nk = int(blockIdx.x) < p.ntiles ? (p.ntiles - int(blockIdx.x) + G - 1) / G : 0;
+  if (nk == 0) return;                      // the whole block: no barrier is left unmatched
+  auto tile_at = [&](int k, int& row, int& j0) {
+    const int t = int(blockIdx.x) + k * G;
+    row = fast_div(t, p.div_nchunk);                     // b * N + i
+    j0 = (t - row * p.nchunk) * K3_TP;
+  };
 
   // ---- wave jobs: output channel block nb, both pair halves ----
   const int nb = wave;
@@ -102,26 +124,68 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   stage_f32(sm.outb, p.ln_out_b, C);
   stage_f32(sm.bp, p.p_out_b, CZ);
   stage_f32(sm.bg, p.g_out_b, CZ);
-  lds_barrier();
 
-  const int N = p.N;
   const size_t ch_stride = size_t(p.B) * N * p.n_pad;
+  const uint32_t xo_bytes = uint32_t(p.B) * uint32_t(N) * uint32_t(N) * uint32_t(CZ) * 2u;
+  const auto rsrc_o = __builtin_amdgcn_make_buffer_rsrc(p.out, 0, xo_bytes, 0x00020000);
 
-  for (int t = blockIdx.x; t < p.ntiles; t += gridDim.x) {
-    const int row = fast_div(t, p.div_nchunk);                      // b * N + i
-    const int j0 = (t - row * p.nchunk) * K3_TP;
+  // y of a tile -> channel-major staging, 128 bytes (64 pairs) per row. Row r
+  // holds channel r ^ ((r >> 1) & 1), so that the even (and the odd) channels
+  // one 16-lane cycle of the transpose reads fall in both halves of the banks.
+  uint32_t yoff[NLD];                       // per-lane byte offsets from the tile's first y element
+#pragma unroll
+  for (int q = 0; q < NLD; ++q) {
+    const int s = (wave * NLD + q) * 64 + lane;          // 16-byte slot
+    const int r = s >> 3, jc = s & 7;
+    const int ch = r ^ ((r >> 1) & 1);
+    yoff[q] = (uint32_t(ch) * uint32_t(ch_stride) + 8u * uint32_t(jc)) * 2u;
+  }
+  auto load_y = [&](int row, int j0) {
+    const char* base = reinterpret_cast<const char*>(p.plane_y + size_t(row) * p.n_pad + j0);
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) load_lds16(base + yoff[q], sm.ys + (wave * NLD + q) * 1024);
+  };
+  // x of a tile -> the z tile, 512 bytes per pair row, 16-byte chunk c of pair
+  // lp at position c ^ (8 (lp & 1)) (conflict-free for the LayerNorm lane
+  // mapping); a pair past N reads pair N - 1 (its results are not stored)
+  auto load_x = [&](int row, int j0) {
+    const char* base = reinterpret_cast<const char*>(p.x + (size_t(row) * N + j0) * CZ);
+    const int last = N - 1 - j0;
+#pragma unroll
+    for (int q = 0; q < NLD; ++q) {
+      const int s = (wave * NLD + q) * 64 + lane;
+      const int pr = s >> 5, pos = s & 31;
+      const int c = pos ^ ((pr & 1) << 3);
+      const uint32_t off = (uint32_t(min(pr, last)) * CZ + 8u * uint32_t(c)) * 2u;
+      load_lds16(base + off, sm.z + (wave * NLD + q) * 1024);
+    }
+  };
 
-    // ---- y -> pair-major LDS rows (two channels per dword) ----
-    // item: channel pair cp = id / 8, pair chunk jc = id % 8 (8 lanes cover
-    // one channel's 128 bytes)
+  {
+    int row, j0;
+    tile_at(0, row, j0);
+    load_y(row, j0);
+    load_x(row, j0);
+  }
+  for (int k = 0; k < nk; ++k) {
+    int row, j0, rown, j0n;
+    tile_at(k, row, j0);
+    tile_at(k + 1 < nk ? k + 1 : k, rown, j0n);      // the last tile loads itself again
+    // y and x of this tile have landed; the previous tile's stores may not have
+    if (k == 0) wait_vm<0>();
+    else wait_vm<NST>();
+    lds_barrier();
+
+    // ---- y staging -> pair-major rows (two channels per dword) ----
+    // item: channel pair cp = id / 8, pair chunk jc = id % 8
 #pragma unroll
     for (int it = 0; it < NY; ++it) {
       const int id = it * K3_THREADS + tid;
       const int cp = id >> 3;
       const int jc = id & 7;
-      const uint16_t* src = p.plane_y + size_t(2 * cp) * ch_stride + size_t(row) * p.n_pad + j0 + 8 * jc;
-      const u32x4 ya = ld16(src);
-      const u32x4 yb = ld16(src + ch_stride);
+      const int flip = cp & 1;              // rows of channels 2 cp, 2 cp + 1 (see load_y)
+      const u32x4 ya = ld16(sm.ys + ((2 * cp) ^ flip) * 128 + 16 * jc);
+      const u32x4 yb = ld16(sm.ys + ((2 * cp + 1) ^ flip) * 128 + 16 * jc);
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const uint32_t even = __builtin_amdgcn_perm(yb[q], ya[q], 0x05040100u);   // pair 8jc + 2q
@@ -131,23 +195,19 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
         *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0 + 1, cp >> 2) + 4 * (cp & 3)) = odd;
       }
     }
-    // ---- x -> LayerNorm_in -> z_in in LDS (pairs past N: zeros) ----
+    // ---- LayerNorm_in in place: x rows of the z tile -> z_in ----
+    // (the 8 lanes of pair lp are in one wave and read the whole row before
+    // any of them writes it)
     {
-      const bool valid = j0 + lp < N;
       u32x4 xr[NV], z[NV];
 #pragma unroll
-      for (int v = 0; v < NV; ++v)
-        xr[v] = valid ? ld16(p.x + (size_t(row) * N + j0 + lp) * CZ + 8 * sub + 64 * v) : u32x4{0, 0, 0, 0};
-      if (valid) {
-        layer_norm_row_lds<NV>(xr, sm.inw, sm.inb, sub, p.eps, z);
-      } else {
-#pragma unroll
-        for (int v = 0; v < NV; ++v) z[v] = u32x4{0, 0, 0, 0};
-      }
+      for (int v = 0; v < NV; ++v) xr[v] = ld16(sm.z + lp * (C * 2) + (((sub + 8 * v) ^ ((lp & 1) << 3)) << 4));
+      layer_norm_row_lds<NV>(xr, sm.inw, sm.inb, sub, p.eps, z);
 #pragma unroll
       for (int v = 0; v < NV; ++v) st16(sm.z + soff<C>(lp, sub + 8 * v), z[v]);
     }
     lds_barrier();
+    load_y(rown, j0n);
 
     // ---- LayerNorm_out in place on the pair rows of y ----
     {
@@ -201,18 +261,20 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
       }
     }
     lds_barrier();
+    load_x(rown, j0n);
 
-    // ---- coalesced pair-major stores of out ----
+    // ---- pair-major stores of out (a pair past N goes past the end of out:
+    // 0x80000000 plus a tile base below 2^31 stays below 2^32, and is dropped) ----
+    const int so = __builtin_amdgcn_readfirstlane((row * N + j0) * CZ * 2);
 #pragma unroll
     for (int it = 0; it < NST; ++it) {
       const int id = it * K3_THREADS + tid;
       const int pr = id / (CZ / 8);
       const int cc = id - pr * (CZ / 8);
-      if (j0 + pr < N) {
-        u32x4 v = ld16(sm.o + pr * (C * 2) + ((cc ^ ((pr & 31) >> 1)) << 4));
-        if (pr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-        st16(p.out + (size_t(row) * N + j0 + pr) * CZ + 8 * cc, v);
-      }
+      u32x4 v = ld16(sm.o + pr * (C * 2) + ((cc ^ ((pr & 31) >> 1)) << 4));
+      if (pr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+      const uint32_t off = j0 + pr < N ? uint32_t(id) * 16u : 0x80000000u;
+      buffer_store16(rsrc_o, v, off + uint32_t(so));
     }
   }
 }

@@ -56,6 +56,23 @@ __device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, const u
 }
 __device__ __forceinline__ bf16x8 ld_frag(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One 16-byte-per-lane global -> LDS copy (direct load, no registers): lane
+// l's 16 bytes land at lds + 16 l; `lds` must be the same for the whole wave.
+// It counts as a vector-memory operation: wait_vm before reading the bytes.
+__device__ __forceinline__ void load_lds16(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
+}
+
+// wait until at most n vector-memory operations of this wave are outstanding
+// (they retire in issue order)
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | 0x0F70);
+}
+
 // One bf16 from global memory. The address-space cast makes it a global load:
 // a flat load also counts against the LDS wait counter, so every later LDS
 // wait or barrier would wait for it too.
