@@ -277,6 +277,9 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
       buffer_store16(rsrc_o, v, off + uint32_t(so));
     }
   }
+  // the last tile's loads of itself: nothing may still be writing the LDS
+  // when the block ends
+  wait_vm<0>();
 }
 
 // ---------------------------------------------------------------------------
