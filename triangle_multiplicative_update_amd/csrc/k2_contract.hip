@@ -338,36 +338,26 @@ __global__ __launch_bounds__(K2_THREADS) void k2_contract_p(const K2Args p) {
       if (kt == 0 && k > 0) wait_vm<K2P_STORES>();
       else wait_vm<0>();
       lds_barrier();
-      if (kt + 1 < nk) issue(kt + 1);
       const uint8_t* st = smem + (kt % C::STAGES) * C::STAGE_BYTES;
-      // fragments in two register sets: sub-step s + 1's LDS reads are issued
-      // before sub-step s's MFMAs, so each read batch has a batch of MFMAs to
-      // land behind; the scheduling groups below keep that order (left to
-      // itself the compiler issues each batch just before its MFMAs and
-      // waits for it there)
-      bf16x8 af[2][C::MI], bfr[2][C::NJ];
-      auto ldf = [&](int s, int b) {
-#pragma unroll
-        for (int mi = 0; mi < C::MI; ++mi) af[b][mi] = ld_frag(st + offA[mi][s]);
-#pragma unroll
-        for (int nj = 0; nj < C::NJ; ++nj) bfr[b][nj] = ld_frag(st + offB[nj][s]);
-      };
-      ldf(0, 0);
+      // The CU's address unit takes the direct loads in issue order, ~2 K
+      // clocks for a step's 64, and a wave stalls until its own are taken.
+      // Waves 0-3 (one per SIMD) issue the next step's fills at the top of
+      // the step; waves 4-7, the SIMDs' second waves, after their first
+      // sub-step of MFMAs, instead of stalling behind waves 0-3's loads with
+      // their matrix cores idle.
+      const int fill_at = wave >= 4 ? 1 : 0;
 #pragma unroll
       for (int s = 0; s < SUB; ++s) {
-        if (s + 1 < SUB) ldf(s + 1, (s + 1) & 1);
+        if (s == fill_at && kt + 1 < nk) issue(kt + 1);
+        bf16x8 af[C::MI], bfr[C::NJ];
+#pragma unroll
+        for (int mi = 0; mi < C::MI; ++mi) af[mi] = ld_frag(st + offA[mi][s]);
+#pragma unroll
+        for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = ld_frag(st + offB[nj][s]);
 #pragma unroll
         for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-          for (int nj = 0; nj < C::NJ; ++nj)
-            acc[mi][nj] = mfma32x32x16(bfr[s & 1][nj], af[s & 1][mi], acc[mi][nj]);
-      }
-      // scheduling groups (0x100: LDS reads, 0x008: MFMAs)
-      __builtin_amdgcn_sched_group_barrier(0x100, C::MI + C::NJ, 0);
-#pragma unroll
-      for (int s = 0; s < SUB; ++s) {
-        if (s + 1 < SUB) __builtin_amdgcn_sched_group_barrier(0x100, C::MI + C::NJ, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, C::MI * C::NJ, 0);
+          for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = mfma32x32x16(bfr[nj], af[mi], acc[mi][nj]);
       }
     }
     lds_barrier();   // every wave is done with the ring
