@@ -297,9 +297,11 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
 //            registers) into the shared y rows; LayerNorm waves write z of
 //            tile k+1
 //   phase 2: matrix waves run the rest of the gate, store tile k-1 and load
-//            y of tile k+3; LayerNorm waves write u of tile k+1 and load x of
-//            tile k+3 (two register sets: a tile's loads have 1.5 iterations
-//            to land).
+//            y of tile k+3; LayerNorm waves write u of tile k+1.
+// The LayerNorm waves load x of tile k+3 in phase 1, right after their
+// LayerNorm_in has read the register set the loads go to (two register sets:
+// x has 2 iterations to land, y 1.5); phase 2 then holds the matrix waves'
+// y loads and stores alone.
 // Loads are issued in every iteration (clamped to the block's last tile) and
 // the stores too (past the end of out where there is nothing to store):
 // vector-memory operations retire in issue order and the compiler counts the
@@ -572,9 +574,9 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
     // with tile k + 3
     auto iteration = [&](int k, auto set) {
       if (k + 1 < nk) ln_in((k + 1) & 1, set);
+      prefetch_x(k + 3, set);
       lds_barrier();
       if (k + 1 < nk) ln_out((k + 1) & 1);
-      prefetch_x(k + 3, set);
       lds_barrier();
     };
     for (int k = 0; k < nit; k += 2) {
