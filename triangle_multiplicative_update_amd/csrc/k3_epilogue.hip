@@ -292,11 +292,10 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
 // wave, writing z and u for the matrix waves. Each SIMD holds one wave of each
 // kind, so the matrix cores of one overlap the vector ALU work of the other.
 // Iteration k has two barriers:
-//   phase 1: matrix waves run tile k's MFMAs (u/z buffer k % 2) and half of
-//            the first pair half's gate, then transpose the y of tile k+1 (in
-//            registers) into the shared y rows; LayerNorm waves write z of
-//            tile k+1
-//   phase 2: matrix waves run the rest of the gate, store tile k-1 and load
+//   phase 1: matrix waves run tile k's MFMAs (u/z buffer k % 2), then
+//            transpose the y of tile k+1 (in registers) into the shared y
+//            rows; LayerNorm waves write z of tile k+1
+//   phase 2: matrix waves run both pair halves' gates, store tile k-1 and load
 //            y of tile k+3; LayerNorm waves write u of tile k+1.
 // The LayerNorm waves load x of tile k+3 in phase 1, right after their
 // LayerNorm_in has read the register set the loads go to (two register sets:
@@ -392,12 +391,10 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
         acc_g = mfma32x32x16(wg[ks], z, acc_g);
       }
     };
-    // sigmoid(g) * p of register groups rg0 .. rg1 - 1 of pair half mb
-    auto gate = [&](int b, int mb, const f32x16& acc_p, const f32x16& acc_g, int rg0, int rg1) {
+    auto gate = [&](int b, int mb, const f32x16& acc_p, const f32x16& acc_g) {
       const int prow = 32 * mb + l32;
 #pragma unroll
       for (int rg = 0; rg < 4; ++rg) {
-        if (rg < rg0 || rg >= rg1) continue;
         float o[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) o[q] = sigmoid_f(acc_g[4 * rg + q]) * acc_p[4 * rg + q];
@@ -485,18 +482,16 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
       const int b = k & 1;
       f32x16 p0, g0, p1, g1;
       if (k < nk) {
-        // the second half's MFMAs overlap half of the first half's gate; the
-        // other half waits for phase 2, which is the LayerNorm waves' longer
-        // phase (phase 1 is the matrix waves' longer one)
+        // both gates wait for phase 2: phase 1, with the transpose, is the
+        // matrix waves' longer phase
         mma(b, 0, p0, g0);
         mma(b, 1, p1, g1);
-        gate(b, 0, p0, g0, 0, 2);
       }
       if (k + 1 < nk) transpose(set);
       lds_barrier();
       if (k < nk) {
-        gate(b, 0, p0, g0, 2, 4);
-        gate(b, 1, p1, g1, 0, 4);
+        gate(b, 0, p0, g0);
+        gate(b, 1, p1, g1);
       }
       store(k - 1);
       prefetch_y(k + 3, set);
