@@ -268,12 +268,18 @@ def _x_f64_rows(x_bits: np.ndarray, b: int, rows) -> np.ndarray:
 
 
 def forward(inp: Dict[str, Optional[np.ndarray]], direction: str, *, eps: float = 1e-5,
-            rounding: str = "kernel", keep_z: bool = False, row_block: int = 64) -> Intermediates:
-    """Whole forward pass on bf16 inputs (bit patterns), chunked by rows of pairs.
+            rounding: str = "kernel", keep_z: bool = False, row_block: int = 64,
+            ch_block: int = 16) -> Intermediates:
+    """Whole forward pass on bf16 inputs (bit patterns).
 
     ``inp`` holds "x" [B,N,N,c_z] (or [N,N,c_z]), optional "mask" [B,N,N] (or
-    [N,N]) and the twelve named parameters, all as bf16 bit patterns.
+    [N,N]) and the twelve named parameters, all as bf16 bit patterns. The
+    pairwise steps run over ``row_block`` rows of pairs at a time and the
+    contraction over ``ch_block`` channels at a time, only to bound memory: every
+    value is computed independently of the blocking.
     """
+    if row_block < 1 or ch_block < 1:
+        raise ValueError("row_block and ch_block must be >= 1")
     if direction not in ("outgoing", "incoming"):
         raise ValueError(f"direction must be 'outgoing' or 'incoming', got {direction!r}")
     if rounding not in ("kernel", "none"):
@@ -301,7 +307,6 @@ def forward(inp: Dict[str, Optional[np.ndarray]], direction: str, *, eps: float 
                 Z[bi, rows] = z
 
     Y = np.empty((B, N, N, c), store_t)
-    ch_block = 16
     for bi in range(B):
         for c0 in range(0, c, ch_block):
             cs = slice(c0, min(c, c0 + ch_block))

@@ -1,8 +1,9 @@
 """Seeded synthetic inputs for the triangle multiplicative update.
 
-This module is shared by the CPU oracle, the GPU tests and the benchmark. It only
-draws random numbers and stores them as bf16 bit patterns; it holds none of the
-operation's arithmetic.
+This module feeds both sides of every comparison: the tests and the benchmark
+draw inputs here and hand the same bits to the CPU oracle and to the GPU library
+(neither of which imports it). It only draws random numbers and stores them as
+bf16 bit patterns; it holds none of the operation's arithmetic.
 
 Distributions follow the workload descriptions for the operation (pair
 representation x ~ N(0, s^2); projection weights ~ N(0, 1/fan_in); biases

@@ -58,6 +58,70 @@ def test_scalar_bf16_helper_against_torch():
     assert np.array_equal(got, ref)
 
 
+def scalar_bf16_decode(bits: int) -> float:
+    """The value of one bf16 bit pattern, from the format's definition: sign bit
+    15, biased exponent bits 14..7 (bias 127), fraction bits 6..0; exponent 0 is
+    +-0 or a subnormal (fraction * 2**-133), exponent 255 is +-inf or NaN."""
+    sign = -1.0 if (bits >> 15) & 1 else 1.0
+    e = (bits >> 7) & 0xFF
+    f = bits & 0x7F
+    if e == 0xFF:
+        return sign * math.inf if f == 0 else math.nan
+    if e == 0:
+        return sign * math.ldexp(f, -133)
+    return sign * math.ldexp(128 + f, e - 127 - 7)
+
+
+def _bits_list(bits):
+    """Nested lists of decoded values (the brute force's own decoding)."""
+    a = np.asarray(bits, dtype=np.uint16)
+    flat = [scalar_bf16_decode(int(b)) for b in a.ravel()]
+    return np.array(flat, dtype=np.float64).reshape(a.shape).tolist()
+
+
+# --------------------------------------------------------------------------- #
+# the oracle's bf16 decoding                                                   #
+# --------------------------------------------------------------------------- #
+
+ALL_BITS = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+
+
+def test_bf16_decode_every_pattern_against_torch():
+    got = oracle.bf16_bits_to_f64(ALL_BITS)
+    ref = torch.from_numpy(ALL_BITS.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert nan.sum() == 2 * 127                      # exponent 255 with a nonzero fraction
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))   # -0 stays -0
+
+
+def test_bf16_decode_every_pattern_against_definition():
+    got = oracle.bf16_bits_to_f64(ALL_BITS)
+    want = np.array([scalar_bf16_decode(int(b)) for b in ALL_BITS])
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+    # a few patterns by hand: 1.0, -2.0, the smallest subnormal, the largest finite
+    spot = {0x3F80: 1.0, 0xC000: -2.0, 0x0001: 2.0 ** -133, 0x7F7F: float.fromhex("0x1.fep127"),
+            0x7F80: math.inf, 0x3F81: 1.0 + 2.0 ** -7}
+    for b, v in spot.items():
+        assert oracle.bf16_bits_to_f64(np.array([b], np.uint16))[0] == v
+
+
+def test_bf16_decode_pin_detects_a_planted_mistake(monkeypatch):
+    """The all-pattern pin fails when the decoder shifts by one bit too few."""
+    def wrong_shift(bits):
+        u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 15
+        return u.view(np.float32).astype(np.float64)
+
+    monkeypatch.setattr(T, "bf16_bits_to_f64", wrong_shift)
+    monkeypatch.setattr(oracle, "bf16_bits_to_f64", wrong_shift)
+    with pytest.raises(AssertionError):
+        test_bf16_decode_every_pattern_against_definition()
+
+
 # --------------------------------------------------------------------------- #
 # P8: the oracle's bf16 rounding                                               #
 # --------------------------------------------------------------------------- #
@@ -124,7 +188,7 @@ def test_bf16_round_matches_scalar_definition_on_f64():
 
 def _brute_force(inp, direction, rounding, eps=1e-5):
     """Scalar loops over every index, written from the formula alone."""
-    f = lambda bits: T.bf16_bits_to_f64(bits).tolist() if bits is not None else None
+    f = lambda bits: _bits_list(bits) if bits is not None else None
     x = f(inp["x"])
     B, N = len(x), len(x[0])
     cz = len(x[0][0][0])
@@ -191,6 +255,11 @@ TINY = [
 ]
 
 
+# the oracle's row and channel blockings: one row / channel at a time, ragged
+# blocks, and the default (one block at these sizes)
+BLOCKINGS = [(rb, cb) for rb in (1, 2, 64) for cb in (1, 3, 16)]
+
+
 @pytest.mark.parametrize("direction", ["outgoing", "incoming"])
 @pytest.mark.parametrize("B,N,c,mask,biases", TINY)
 def test_brute_force_kernel_rounding(direction, B, N, c, mask, biases):
@@ -198,14 +267,84 @@ def test_brute_force_kernel_rounding(direction, B, N, c, mask, biases):
                    seed=N * 7 + c)
     inp = si.generate(wl)
     Z, A, Bv, Y, OUT = _brute_force(inp, direction, "kernel")
+    for rb, cb in BLOCKINGS:
+        r = oracle.forward(inp, direction, rounding="kernel", keep_z=True, row_block=rb,
+                           ch_block=cb)
+        # bf16 stages agree bitwise (scalar sums and BLAS sums differ only far
+        # below a bf16 ulp); the unrounded output agrees to fp64 rounding noise.
+        assert np.array_equal(r.z, Z), (rb, cb)
+        assert np.array_equal(r.a, A), (rb, cb)
+        assert np.array_equal(r.b, Bv), (rb, cb)
+        assert np.array_equal(r.y, Y), (rb, cb)
+        np.testing.assert_allclose(r.out, OUT, rtol=1e-12, atol=1e-13, err_msg=f"{(rb, cb)}")
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_two_dimensional_mask(direction):
+    """A [N, N] mask at B = 1 is the [1, N, N] mask (brute force on both)."""
+    wl = si.custom(1, 6, 4, mask="bernoulli", mask_p=0.6, seed=44)
+    inp = si.generate(wl)
+    Z, A, Bv, Y, OUT = _brute_force(inp, direction, "kernel")
+    inp2 = dict(inp)
+    inp2["mask"] = inp["mask"][0]
+    assert inp2["mask"].ndim == 2
+    for rb, cb in ((64, 16), (1, 3)):
+        r = oracle.forward(inp2, direction, keep_z=True, row_block=rb, ch_block=cb)
+        assert np.array_equal(r.a, A) and np.array_equal(r.b, Bv) and np.array_equal(r.y, Y)
+        np.testing.assert_allclose(r.out, OUT, rtol=1e-12, atol=1e-13)
+    # batchless x with a [N, N] mask as well
+    inp3 = dict(inp2)
+    inp3["x"] = inp["x"][0]
+    r3 = oracle.forward(inp3, direction)
+    assert np.array_equal(r3.y, Y)
+
+
+def _formula_torch(inp, direction, rnd=None):
+    """The formula with torch fp64 library routines (layer_norm, linear, sigmoid,
+    einsum), written independently of the oracle; ``rnd`` is applied at the
+    rounding points when given."""
+    r = rnd or (lambda t: t)
+    f = lambda k: None if inp.get(k) is None else torch.tensor(_bits_list(inp[k]), dtype=torch.float64)
+    x, m = f("x"), f("mask")
+    cz = x.shape[-1]
+    c = inp["p_in_weight"].shape[0] // 2
+    e = float(np.float32(1e-5))
+    z = r(torch.nn.functional.layer_norm(x, (cz,), f("norm_in_weight"), f("norm_in_bias"), eps=e))
+    p = torch.nn.functional.linear(z, f("p_in_weight"), f("p_in_bias"))
+    g = torch.sigmoid(torch.nn.functional.linear(z, f("g_in_weight"), f("g_in_bias")))
+    gp = g * p * (torch.ones(x.shape[:-1], dtype=torch.float64) if m is None else m)[..., None]
+    a, b = r(gp[..., :c] + 0.0), r(gp[..., c:] + 0.0)
+    eq = "bikc,bjkc->bijc" if direction == "outgoing" else "bkic,bkjc->bijc"
+    y = r(torch.einsum(eq, a, b))
+    u = r(torch.nn.functional.layer_norm(y, (c,), f("norm_out_weight"), f("norm_out_bias"), eps=e))
+    out = torch.sigmoid(torch.nn.functional.linear(z, f("g_out_weight"), f("g_out_bias"))) * \
+        torch.nn.functional.linear(u, f("p_out_weight"), f("p_out_bias"))
+    return z, a, b, y, out
+
+
+def _torch_bf16(t):
+    """One-step fp64 -> bf16 rounding with the scalar definition (test side)."""
+    flat = [scalar_bf16(v) for v in t.reshape(-1).tolist()]
+    return torch.tensor(flat, dtype=torch.float64).reshape(t.shape)
+
+
+@pytest.mark.parametrize("direction", ["outgoing", "incoming"])
+def test_blocked_forward_against_library_formula(direction):
+    """Several row blocks and ragged channel blocks (N = 70 > 64 rows, c = 20 >
+    16 channels by default) against torch's fp64 routines, without rounding and
+    with the rounding points applied by the scalar rounding definition."""
+    wl = si.custom(1, 70, 20, mask="bernoulli", mask_p=0.8, seed=45)
+    inp = si.generate(wl)
+    z, a, b, y, out = _formula_torch(inp, direction)
+    for rb, cb in ((64, 16), (16, 6)):
+        r = oracle.forward(inp, direction, rounding="none", keep_z=True, row_block=rb, ch_block=cb)
+        for got, want in ((r.z, z), (r.a, a), (r.b, b), (r.y, y), (r.out, out)):
+            np.testing.assert_allclose(got, want.numpy(), rtol=1e-11, atol=1e-12)
+    z, a, b, y, out = _formula_torch(inp, direction, rnd=_torch_bf16)
     r = oracle.forward(inp, direction, rounding="kernel", keep_z=True)
-    # bf16 stages agree bitwise (scalar sums and BLAS sums differ only far below
-    # a bf16 ulp); the unrounded output agrees to fp64 rounding noise.
-    assert np.array_equal(r.z, Z)
-    assert np.array_equal(r.a, A)
-    assert np.array_equal(r.b, Bv)
-    assert np.array_equal(r.y, Y)
-    np.testing.assert_allclose(r.out, OUT, rtol=1e-12, atol=1e-13)
+    for got, want in ((r.z, z), (r.a, a), (r.b, b), (r.y, y)):
+        assert np.array_equal(got, want.numpy())
+    np.testing.assert_allclose(r.out, out.numpy(), rtol=1e-11, atol=1e-12)
 
 
 @pytest.mark.parametrize("direction", ["outgoing", "incoming"])
