@@ -33,8 +33,12 @@ def _ensure_library():
     """Build libtrimul.so only when nothing is built (normally build() ran first)."""
     lib = os.path.join(ROOT, "triangle_multiplicative_update_amd", "libtrimul.so")
     if not os.path.exists(lib):
-        from triangle_multiplicative_update_amd.build import build
-        build()
+        import importlib.util
+        path = os.path.join(ROOT, "triangle_multiplicative_update_amd", "build.py")
+        spec = importlib.util.spec_from_file_location("_trimul_build", path)
+        mod = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(mod)
+        mod.build()
 
 
 _ensure_library()
