@@ -139,6 +139,36 @@ int trimul_forward_stage(int stage,
                          int B, int N, int c_z, int c, int direction, float eps,
                          void* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/* ---- Allocation-free forward, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, and harnesses
+ * that forbid hipMalloc. ----
+ *
+ * The same computation, checks and kernels as trimul_forward, with the a, b
+ * and y planes kept in a fixed device array inside the library instead of a
+ * caller workspace: TRIMUL_NOALLOC_SCRATCH_BYTES (64 MiB) per GPU, reserved
+ * when the library's device code is loaded on that GPU and held until the
+ * process ends. The caller still passes every input and `out`. Calls whose
+ * planes (trimul_workspace_bytes(B, N, c, direction)) exceed that size are
+ * declined with TRIMUL_E_UNSUPPORTED before any launch (c = 128, B = 1 is
+ * served up to N = 273; c = 256, B = 1 up to N = 192); use trimul_forward then.
+ * No allocation and no synchronization happen on any call; the first call on
+ * a device also looks up that device's copy of the array (not a stream
+ * operation). The array keeps the last call's planes; no part of it needs to
+ * start at zero. Every call on one GPU shares that GPU's array: calls that
+ * overlap in time on one GPU (different streams or host threads without
+ * ordering between them) race and give undefined results. */
+#define TRIMUL_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+int trimul_forward_noalloc(const void* x, const void* mask,
+                           const void* norm_in_w, const void* norm_in_b,
+                           const void* p_in_w, const void* p_in_b,
+                           const void* g_in_w, const void* g_in_b,
+                           const void* norm_out_w, const void* norm_out_b,
+                           const void* p_out_w, const void* p_out_b,
+                           const void* g_out_w, const void* g_out_b,
+                           int B, int N, int c_z, int c, int direction, float eps,
+                           void* out, void* stream);
+
 /* ---- Captured forward (same page, "Prepared class API": make_cuda_graph,
  * "one graph launch per call for these buffers"; the small-N calls are host
  * bound when launched eagerly). ----

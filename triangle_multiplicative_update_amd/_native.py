@@ -34,6 +34,7 @@ SIGNATURES = {
     "trimul_validate": (_i, _TENSOR_ARGS + [_i, _i, _i, _i, _i, _f, _vp, _vp, _sz]),
     "trimul_forward": (_i, _TENSOR_ARGS + [_i, _i, _i, _i, _i, _f, _vp, _vp, _sz, _vp]),
     "trimul_forward_stage": (_i, [_i] + _TENSOR_ARGS + [_i, _i, _i, _i, _i, _f, _vp, _vp, _sz, _vp]),
+    "trimul_forward_noalloc": (_i, _TENSOR_ARGS + [_i, _i, _i, _i, _i, _f, _vp, _vp]),
     "trimul_graph_create": (_i, _TENSOR_ARGS + [_i, _i, _i, _i, _i, _f, _vp, _vp, _sz,
                                                 ctypes.POINTER(_vp)]),
     "trimul_graph_launch": (_i, [_vp, _vp]),
@@ -45,7 +46,7 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build the gfx950 library first "
-            "(python -m triangle_multiplicative_update_amd.build)")
+            "(python triangle_multiplicative_update_amd/build.py)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

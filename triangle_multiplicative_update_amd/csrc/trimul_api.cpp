@@ -276,6 +276,46 @@ int run(int first_stage, int last_stage, const void* x, const void* mask, const 
   return ok();
 }
 
+// ---- fixed device scratch for trimul_forward_noalloc ----
+//
+// The a, b and y planes of the allocation-free entry point live in this
+// file-scope device array, one copy per GPU, held until the process ends. In
+// host code `scratch` names a host-side stand-in, not a device address: the
+// device address is taken once per device with hipGetSymbolAddress (with that
+// device current) and only that pointer is ever passed to the kernels.
+constexpr size_t kScratchBytes = size_t(TRIMUL_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+void* g_scratch_ptr[kMaxDevices] = {};
+std::mutex g_scratch_mu;
+
+// The current device's copy of `scratch` (looked up on the first call per
+// device and kept); nullptr with the reason in g_err on failure.
+void* scratch_for_current_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    fail(TRIMUL_E_DEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    fail(TRIMUL_E_DEVICE, "device index %d out of range", dev);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      fail(TRIMUL_E_DEVICE, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+           hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 struct trimul_graph_s {
@@ -341,6 +381,30 @@ int trimul_forward_stage(int stage, const void* x, const void* mask, const void*
   return run(stage, stage, x, mask, norm_in_w, norm_in_b, p_in_w, p_in_b, g_in_w, g_in_b,
              norm_out_w, norm_out_b, p_out_w, p_out_b, g_out_w, g_out_b, B, N, c_z, c, direction,
              eps, out, workspace, workspace_bytes, stream);
+}
+
+int trimul_forward_noalloc(const void* x, const void* mask, const void* norm_in_w,
+                           const void* norm_in_b, const void* p_in_w, const void* p_in_b,
+                           const void* g_in_w, const void* g_in_b, const void* norm_out_w,
+                           const void* norm_out_b, const void* p_out_w, const void* p_out_b,
+                           const void* g_out_w, const void* g_out_b, int B, int N, int c_z, int c,
+                           int direction, float eps, void* out, void* stream) {
+  int st = check_shape(B, N, c_z, c, direction);
+  if (st != TRIMUL_OK) return st;
+  const size_t need = trimul_workspace_bytes(B, N, c, direction);
+  if (need > kScratchBytes)
+    return fail(TRIMUL_E_UNSUPPORTED,
+                "B=%d, N=%d, c=%d needs %zu bytes of planes, above the %zu-byte fixed scratch of "
+                "trimul_forward_noalloc; call trimul_forward with a workspace",
+                B, N, c, need, kScratchBytes);
+  DeviceInfo info;
+  st = current_device_check(info);
+  if (st != TRIMUL_OK) return st;
+  void* ws = scratch_for_current_device();
+  if (ws == nullptr) return TRIMUL_E_DEVICE;
+  return run(1, 3, x, mask, norm_in_w, norm_in_b, p_in_w, p_in_b, g_in_w, g_in_b, norm_out_w,
+             norm_out_b, p_out_w, p_out_b, g_out_w, g_out_b, B, N, c_z, c, direction, eps, out,
+             ws, kScratchBytes, stream);
 }
 
 int trimul_graph_create(const void* x, const void* mask, const void* norm_in_w,
