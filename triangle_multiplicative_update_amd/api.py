@@ -62,6 +62,13 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
 
+def _as_stream(stream, device) -> torch.cuda.Stream:
+    """A torch stream object for a torch stream or a raw hipStream_t handle."""
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=device)
+
+
 def _prep_param(name, t, precision, device):
     if t is None:
         return None
@@ -101,6 +108,22 @@ def triangle_multiplicative_update(
                                   f"(served: None, 'default', 'none', 'bfloat16')")
     if not isinstance(x, torch.Tensor):
         raise ValueError("x must be a tensor")
+    if x.device.type == "cuda" and stream is not None:
+        # Every cast, allocation and launch of the call goes on the caller's
+        # stream, after the work already queued on torch's current stream
+        # (which may have produced the inputs); memory allocated here then
+        # belongs to that stream's pool and is not handed to another stream
+        # while the kernels still use it.
+        ext = _as_stream(stream, x.device)
+        cur = torch.cuda.current_stream(x.device)
+        if ext != cur:
+            ext.wait_stream(cur)
+        with torch.cuda.stream(ext):
+            return triangle_multiplicative_update(
+                x, direction, mask, norm_in_weight, norm_in_bias, p_in_weight, p_in_bias,
+                g_in_weight, g_in_bias, norm_out_weight, norm_out_bias, p_out_weight, p_out_bias,
+                g_out_weight, g_out_bias, eps, precision, out=out, stream=None,
+                workspace=workspace, _stage=_stage)
     params = dict(zip(_PARAM_ORDER, (norm_in_weight, norm_in_bias, p_in_weight, p_in_bias,
                                       g_in_weight, g_in_bias, norm_out_weight, norm_out_bias,
                                       p_out_weight, p_out_bias, g_out_weight, g_out_bias)))
@@ -174,12 +197,7 @@ def triangle_multiplicative_update(
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
     ws_bytes = workspace.numel() * workspace.element_size()
 
-    if stream is None:
-        stream_h = torch.cuda.current_stream(device).cuda_stream
-    elif isinstance(stream, torch.cuda.Stream):
-        stream_h = stream.cuda_stream
-    else:
-        stream_h = int(stream)
+    stream_h = torch.cuda.current_stream(device).cuda_stream
 
     args = [_ptr(xb), _ptr(mask)] + [_ptr(params[n]) for n in _PARAM_ORDER] + \
         [B, N, c_z, c, code, float(eps), _ptr(out_t), workspace.data_ptr(), ws_bytes, stream_h]

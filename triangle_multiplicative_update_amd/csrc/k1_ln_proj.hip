@@ -161,12 +161,19 @@ __global__ __launch_bounds__(K1_THREADS) void k1_ln_proj(const K1Args p) {
     u32x4 z[NV];
     if constexpr (kWide) {
       // (zeroing the x of pairs past N keeps this form's register
-      // allocation free of spills)
+      // allocation free of spills). A zero row has variance 0: with eps = 0
+      // its z would be 0 * inf = NaN, and NaN * (m = 0) stays NaN in the
+      // padded plane columns, which every contraction sum reads. Those pairs
+      // take eps = 1 instead (z = the LayerNorm bias, finite), so their a and
+      // b are +0.0 for any eps >= 0.
       u32x4 xin[NV];
 #pragma unroll
       for (int v = 0; v < NV; ++v) xin[v] = xok ? xr[v] : u32x4{0, 0, 0, 0};
-      layer_norm_row_lds<NV>(xin, sm.lnw, sm.lnb, sub, p.eps, z);
+      layer_norm_row_lds<NV>(xin, sm.lnw, sm.lnb, sub, xok ? p.eps : 1.0f, z);
     } else {
+      // pairs past N repeat pair N - 1 of the same plane row: their z is
+      // non-finite only where that real pair's is, and then the formula's
+      // sums over the row are not finite either
       layer_norm_row<NV>(xr, lnw, lnb, p.eps, z);
     }
 #pragma unroll
