@@ -107,6 +107,36 @@ def stats(gpu: np.ndarray, ref: np.ndarray) -> dict:
     }
 
 
+def assert_within_tolerance_slabs(gpu_slabs, ref_slabs, label: str) -> dict:
+    """The same bar as assert_within_tolerance over every cell of an output
+    given as matching slabs (iterables of arrays), without holding the whole
+    difference in memory; the tail allowance is that of the whole output."""
+    cells = tight = hard = nonfinite = 0
+    sq_diff = sq_ref = 0.0
+    max_abs = 0.0
+    for g, r in zip(gpu_slabs, ref_slabs):
+        s = stats(g, r)
+        g = np.asarray(g, np.float64)
+        r = np.asarray(r, np.float64)
+        cells += s["cells"]
+        tight += s["tight_fail"]
+        hard += s["hard_fail"]
+        nonfinite += s["nonfinite"]
+        sq_diff += float(np.sum((g - r) ** 2))
+        sq_ref += float(np.sum(r ** 2))
+        max_abs = max(max_abs, s["max_abs"])
+    rel = float(np.sqrt(sq_diff) / max(np.sqrt(sq_ref), 1e-300))
+    allowed = math.floor(TAIL_PER_MILLION * 1e-6 * cells)
+    summary = {"cells": cells, "rel_rms": rel, "tight_fail": tight, "hard_fail": hard,
+               "max_abs": max_abs, "nonfinite": nonfinite}
+    say(f"[parity] {label}: {summary} (tail allowance {allowed})")
+    assert nonfinite == 0, f"{label}: non-finite outputs {summary}"
+    assert rel <= REL_RMS_MAX, f"{label}: relative RMS {rel:.3e} > {REL_RMS_MAX}"
+    assert hard == 0, f"{label}: {hard} cells beyond 2e-2 + |ref|/64"
+    assert tight <= allowed, f"{label}: {tight} cells beyond 4e-3 + |ref|/64 (allowed {allowed})"
+    return summary
+
+
 def assert_within_tolerance(gpu, ref, label: str, sampled: bool = False) -> dict:
     s = stats(gpu, ref)
     allowed = math.ceil(TAIL_PER_MILLION * 1e-6 * s["cells"]) if sampled else \

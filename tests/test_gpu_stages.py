@@ -26,6 +26,28 @@ def _ws(B, N, c, direction, device, fill=None):
     return ws
 
 
+def _z_flip_bound(inp, z, half):
+    """Per-channel bound on how far a or b (rows [half*c, half*c + c) of the
+    in-projections) moves when one element q of a pair's z_in takes the
+    neighbouring bf16 value (the GPU's fp32 LayerNorm and the oracle's fp64
+    one can round a z element to different sides of a midpoint).
+
+    a = sigmoid(G) P m with P = z p^T + p_b, G = z g^T + g_b and 0 <= m <= 1; a
+    change dz in z_q moves P by p[ch, q] dz and G by g[ch, q] dz, and sigmoid
+    has slope at most 1/4, so |da| <= (|p[ch, q]| + |P| |g[ch, q]| / 4) |dz|,
+    with |dz| at most the largest ulp of any z element."""
+    f = oracle.bf16_bits_to_f64
+    c = inp["p_in_weight"].shape[0] // 2
+    rows = slice(half * c, half * c + c)
+    p_w, g_w = f(inp["p_in_weight"])[rows], f(inp["g_in_weight"])[rows]
+    p_b = np.zeros(c) if inp["p_in_bias"] is None else f(inp["p_in_bias"])[rows]
+    zz = np.asarray(z, np.float64).reshape(-1, z.shape[-1])
+    P_max = np.abs(zz @ p_w.T + p_b).max(axis=0)                          # [c]
+    az = np.abs(zz[zz != 0])
+    ulp_max = float(np.exp2(np.floor(np.log2(az.max())) - 7)) if az.size else 0.0
+    return (np.abs(p_w).max(axis=1) + P_max * np.abs(g_w).max(axis=1) / 4) * ulp_max
+
+
 @pytest.mark.parametrize("direction", ["outgoing", "incoming"])
 @pytest.mark.parametrize("B,N,c", [(1, 136, 128), (2, 77, 128), (1, 72, 256)])
 def test_planes_match_oracle(gpu, direction, B, N, c):
@@ -37,32 +59,43 @@ def test_planes_match_oracle(gpu, direction, B, N, c):
     with torch.no_grad():
         out = call(d, direction, workspace=ws)
     torch.cuda.synchronize()
-    ref = oracle.forward(inp, direction)
+    ref = oracle.forward(inp, direction, keep_z=True)
     pa, pb, py = planes(ws, B, N, c)
-    report = {}
-    for name, plane, want in (("a", pa, ref.a), ("b", pb, ref.b), ("y", py, ref.y)):
-        got = bf16_to_f64(plane[:, :, :N])
+    got = {}
+    for half, (name, plane, want) in enumerate((("a", pa, ref.a), ("b", pb, ref.b))):
+        g = bf16_to_f64(plane[:, :, :N])
+        got[name] = g
         exp = plane_layout(want, direction, name).astype(np.float64)
-        scale = float(np.sqrt(np.mean(exp ** 2)))
-        diff = np.abs(got - exp)
+        diff = np.abs(g - exp)
         frac = np.count_nonzero(diff) / diff.size
-        # fp32 (GPU) vs fp64 (oracle) before the single rounding: a difference is
-        # one bf16 ulp of the value (2^-7 relative at most), or the effect of a
-        # one-ulp flip of a z_in element of the same pair (|w| * ulp(z), a few
-        # 1e-3 of the plane's scale), rare either way. y also inherits the flips
-        # of a and b through the contraction.
-        rel, floor, max_frac = (2.0 ** -7, 1e-2, 1e-2) if name != "y" else (2.0 ** -6, 1e-2, 0.2)
-        worst = float(np.max(diff - (rel * np.abs(exp) + floor * scale)))
-        report[name] = (frac, worst, max_frac)
-        say(f"[planes] {name}: mismatch fraction {frac:.2e}, worst excess {worst:.3e} (scale {scale:.3e})")
-        if name != "y":
-            n_pad = plane.shape[-1]
-            if n_pad > N:   # padded plane columns are written as +0.0
-                tail = plane[:, :, N:].float().cpu().numpy()
-                assert np.all(tail == 0) and not np.any(np.signbit(tail)), name
-    for name, (frac, worst, max_frac) in report.items():
-        assert worst <= 0, (name, report)
-        assert frac <= max_frac, (name, report)
+        # Before its one rounding the GPU's a is fp32, the oracle's fp64: where
+        # they round apart the results are one bf16 ulp apart (<= 2^-7 |a|).
+        # Where a z element rounded apart, _z_flip_bound applies, twice (two
+        # flipped elements in one pair: about 3e-5 of the pairs at the
+        # measured flip rates; three: about 1e-7).
+        bound = 2.0 ** -7 * np.abs(exp) + 2 * _z_flip_bound(inp, ref.z, half)[:, None, None]
+        worst = float(np.max(diff - bound))
+        say(f"[planes] {name}: mismatch fraction {frac:.2e}, worst excess {worst:.3e}")
+        assert worst <= 0, name
+        assert frac <= 1e-2, name
+        n_pad = plane.shape[-1]
+        if n_pad > N:   # padded plane columns are written as +0.0
+            tail = plane[:, :, N:].float().cpu().numpy()
+            assert np.all(tail == 0) and not np.any(np.signbit(tail)), name
+    # y against the contraction of the GPU's own a and b planes: the products of
+    # bf16 values are exact in fp32, so in any summation order the fp32 sum is
+    # within gamma_N sum_k |a_k b_k| of the exact one (gamma_N = N u / (1 - N u),
+    # u = 2^-24), and the one bf16 rounding adds at most 2^-8 of the value.
+    A = got["a"].reshape(c, B, N, N)
+    Bp = got["b"].reshape(c, B, N, N)
+    Y = A @ np.swapaxes(Bp, -1, -2)
+    S = np.abs(A) @ np.swapaxes(np.abs(Bp), -1, -2)
+    gam = N * 2.0 ** -24 / (1 - N * 2.0 ** -24)
+    y_got = bf16_to_f64(py[:, :, :N]).reshape(c, B, N, N)
+    bound = gam * S + 2.0 ** -8 * (np.abs(Y) + gam * S)
+    worst = float(np.max(np.abs(y_got - Y) - bound))
+    say(f"[planes] y: worst excess over the contraction of the GPU planes {worst:.3e}")
+    assert worst <= 0
     # the output itself
     assert_within_tolerance(bf16_to_f64(out), ref.out, f"{wl.name} {direction}")
 
