@@ -19,6 +19,20 @@ import os
 import sys
 import time
 
+
+def _host_threads():
+    """(cores this process may run on, threads the CPU baseline's BLAS uses):
+    the affinity set, capped by an OMP_NUM_THREADS the environment sets."""
+    aff = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    return aff, (min(aff, int(env)) if env.isdigit() and int(env) > 0 else aff)
+
+
+# BLAS reads its thread count when numpy is first imported: set it first
+AFFINITY_CORES, CPU_THREADS = _host_threads()
+for _v in ("OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS", "BLIS_NUM_THREADS"):
+    os.environ.setdefault(_v, str(CPU_THREADS))
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -33,6 +47,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="before the warm-up, untimed calls until this much GPU time has passed and "
+                         "the time per call has stopped falling (at most 10x this)")
     ap.add_argument("--workload", default=None, help="workload name (default: the N=768 one)")
     ap.add_argument("--direction", default="outgoing", choices=["outgoing", "incoming"])
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
@@ -61,6 +78,44 @@ def measured_traffic(stage: int, workload: str, direction: str, profile_dir: str
     return rec.get("hbm_bytes_per_launch")
 
 
+def measured_trace(stage: int, workload: str, direction: str, profile_dir: str = PROFILE_DIR):
+    """Average device time (us) of a stage kernel over the timed calls of the
+    committed rocprofv3 kernel trace of this workload, if that trace was taken
+    on the current kernel source; else None."""
+    path = os.path.join(profile_dir, f"kernel_trace_{workload}_{direction}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    k = rec.get("kernels", {}).get(KERNEL_NAMES[stage], {})
+    if k.get("kernel_sha") != kernel_sha(stage):
+        return None
+    return k.get("timed_us")
+
+
+def settle(call, min_ms: float):
+    """Untimed calls, in groups of 10, until at least min_ms of GPU time has
+    passed and a group's time per call is within 2 % of the previous group's
+    (at most 10 * min_ms): the clock and power state the timed calls see.
+    Returns (calls, GPU ms, ms per call of the last group)."""
+    import torch
+    total, calls, prev, per = 0.0, 0, None, None
+    while True:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            call()
+        e1.record()
+        e1.synchronize()
+        ms = e0.elapsed_time(e1)
+        total += ms
+        calls += 10
+        per = ms / 10
+        if total >= 10 * min_ms or (total >= min_ms and prev is not None and abs(per - prev) <= 0.02 * prev):
+            return calls, total, per
+        prev = per
+
+
 def cpu_baseline(inp, wl, direction, flops_per_call, sample_rows: int, min_seconds: float = 10.0):
     import numpy as np
     try:
@@ -68,7 +123,7 @@ def cpu_baseline(inp, wl, direction, flops_per_call, sample_rows: int, min_secon
         threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
                       or [1])
     except Exception:
-        threads = 1
+        threads = CPU_THREADS
     import oracle
     # the sample is run whole, again and again, until min_seconds have passed
     runs = 0
@@ -93,6 +148,7 @@ def cpu_baseline(inp, wl, direction, flops_per_call, sample_rows: int, min_secon
         "value": flops_per_call * frac / dt / 1e12,
         "unit": "TFLOP/s",
         "cores": int(threads),
+        "affinity_cores": AFFINITY_CORES,
         "kind": "oracle",
         "sample": sample,
         "seconds": dt,
@@ -143,6 +199,7 @@ def main():
     prep = Prepared(d["x"], direction, d["mask"], {k: d[k] for k in si.PARAM_NAMES}, out, ws)
 
     with torch.no_grad():
+        settle_calls, settle_ms, settle_per_call = settle(prep.forward, args.settle_ms)
         for _ in range(args.warmup):
             prep.forward()
         torch.cuda.synchronize()
@@ -199,6 +256,14 @@ def main():
     roof["traffic"] = measured_traffic(dom + 1, name, direction, args.profile_dir or PROFILE_DIR)
     roof["kernel"] = KERNEL_NAMES[dom + 1]
     roof["kernel_us"] = per_stage_ms[dom] * 1e3
+    # the same kernel's average in the committed rocprofv3 trace (kernel time
+    # alone, without the launch gap the HIP events also hold), and the
+    # fraction it gives
+    tr = measured_trace(dom + 1, name, direction, args.profile_dir or PROFILE_DIR)
+    roof["trace_kernel_us"] = tr
+    if tr:
+        work = sb[dom] / 1e9 if roof["bound"] == "hbm" else sf[dom] / 1e12
+        roof["trace_frac"] = work / (tr * 1e-6) / roof["peak"]
     roof["algorithmic_bytes"] = sb[dom]
     roof["algorithmic_flops"] = sf[dom]
 
@@ -224,6 +289,9 @@ def main():
         "per_stage_us": {KERNEL_NAMES[s + 1]: per_stage_ms[s] * 1e3 for s in range(3)},
         "device_ms_per_step": span_ms,
         "graph_ms_per_step": graph_wall * 1e3 / K,
+        "settle_calls": settle_calls,
+        "settle_gpu_ms": settle_ms,
+        "settle_ms_per_call": settle_per_call,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -12,6 +12,8 @@ import os
 import re
 import types
 
+import pytest
+
 from triangle_multiplicative_update_amd import perf_model, profiling
 
 
@@ -105,3 +107,54 @@ def test_phase_means_split_dispatches_in_start_order(tmp_path):
     for s in (1, 2, 3):
         for p, ph in enumerate(("warmup", "timed", "graph warmup", "graph")):
             assert pm[s][ph] == (1000 * s + 100 * p) / 1e3
+
+
+def test_phase_means_with_settle_steps(tmp_path):
+    settle, warmup, steps = 4, 2, 3
+    names = {1: "void trimul::(anonymous namespace)::k1_ln_proj<128>(trimul::K1Args)",
+             2: "trimul::k2_contract_p(trimul::K2Args)",
+             3: "trimul::(anonymous namespace)::k3_epilogue_ws(trimul::K3Args)"}
+    rows, t = [], 0
+    for p, n in enumerate((settle, warmup, steps, warmup, steps)):
+        for _ in range(n):
+            for s in (1, 2, 3):
+                rows.append({"Kernel_Name": names[s], "Start_Timestamp": t,
+                             "End_Timestamp": t + 1000 * s + 100 * p})
+                t += 10000
+    os.makedirs(tmp_path / "tr")
+    with open(tmp_path / "tr" / "run_kernel_trace.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        w.writeheader()
+        w.writerows(rows)
+    pm = profiling.phase_means(str(tmp_path / "tr"), warmup, steps, settle)
+    for s in (1, 2, 3):
+        for p, ph in enumerate(profiling.PHASES):
+            assert pm[s][ph] == (1000 * s + 100 * p) / 1e3
+    with pytest.raises(ValueError, match="dispatches"):
+        profiling.phase_means(str(tmp_path / "tr"), warmup, steps)      # settle steps not counted
+
+
+def test_util_records_per_stage(tmp_path):
+    names = {1: "void trimul::(anonymous namespace)::k1_ln_proj<128>(trimul::K1Args)",
+             2: "trimul::k2_contract_p(trimul::K2Args)",
+             3: "trimul::(anonymous namespace)::k3_epilogue_ws(trimul::K3Args)"}
+    os.makedirs(tmp_path / "pmc")
+    with open(tmp_path / "pmc" / "run_counter_collection.csv", "w", newline="") as fh:
+        w = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for rep in range(3):
+            for s in (1, 2, 3):
+                w.writerow({"Kernel_Name": names[s], "Counter_Name": "MfmaUtil", "Counter_Value": 10 * s + rep})
+                w.writerow({"Kernel_Name": names[s], "Counter_Name": "VALUBusy", "Counter_Value": 5 * s})
+                w.writerow({"Kernel_Name": names[s], "Counter_Name": "MfmaFlopsBF16", "Counter_Value": 1e9 * s})
+        w.writerow({"Kernel_Name": profiling.COPY_KERNEL, "Counter_Name": "MfmaUtil", "Counter_Value": 99})
+    args = types.SimpleNamespace(pmc=str(tmp_path / "pmc"), workload="n768_c128_pad700",
+                                 direction="outgoing", out=str(tmp_path), bench_args="--steps 3")
+    profiling.util(args)
+    rec = json.load(open(tmp_path / "util_n768_c128_pad700_outgoing.json"))
+    for s in (1, 2, 3):
+        k = rec["kernels"][profiling.KERNEL_NAMES[s]]
+        assert k["mfma_util_pct"] == 10 * s + 1           # median of the three dispatches
+        assert k["valu_busy_pct"] == 5 * s and k["mfma_flops_bf16"] == 1e9 * s
+        assert k["kernel_sha"] == profiling.kernel_sha(s)
+    assert "MfmaUtil" in rec["command"]

@@ -9,7 +9,10 @@ Two kinds of record:
   kernel (``traffic_<kernel>_<workload>_<direction>.json``) carries the bytes
   and a hash of the kernel sources, so ``bench.py`` only reports them while
   the kernel is unchanged, plus a Markdown summary.
-* A kernel-trace summary (``--kernel-trace --stats``) as Markdown.
+* A kernel-trace summary (``--kernel-trace --stats``) as Markdown, with the
+  per-kernel averages of the timed calls and the source hashes as JSON.
+* Matrix-core and vector-ALU utilisation per kernel (``--pmc MfmaUtil
+  VALUBusy MfmaFlopsBF16``), as JSON and Markdown.
 
 Usage (each counter pass is a separate rocprofv3 run; see the written
 summaries for the exact commands)::
@@ -152,24 +155,32 @@ def traffic(args) -> None:
         fh.write("\n".join(md))
 
 
-def phase_means(trace_dir: str, warmup: int, steps: int):
+PHASES = ("settle", "warmup", "timed", "graph warmup", "graph")
+
+
+def phase_means(trace_dir: str, warmup: int, steps: int, settle: int = 0):
     """Mean duration (us) of each stage kernel in each phase of a bench.py run.
 
-    bench.py runs ``warmup`` eager steps, ``steps`` timed eager steps (HIP
-    events between the stages), then ``warmup`` and ``steps`` launches of the
-    captured graph; every step dispatches each stage kernel once, so the
-    dispatches of a stage, in start order, split into those four phases."""
+    bench.py runs ``settle`` untimed eager steps, ``warmup`` eager steps,
+    ``steps`` timed eager steps (HIP events between the stages), then
+    ``warmup`` and ``steps`` launches of the captured graph; every step
+    dispatches each stage kernel once, so the dispatches of a stage, in start
+    order, split into those five phases (a phase of no steps is left out)."""
     durs: dict[int, list] = {1: [], 2: [], 3: []}
     for r in _csv_rows(trace_dir, "kernel_trace.csv"):
         s = stage_of(r["Kernel_Name"])
         if s is not None:
             durs[s].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
-    bounds = {"warmup": (0, warmup), "timed": (warmup, warmup + steps),
-              "graph warmup": (warmup + steps, 2 * warmup + steps), "graph": (2 * warmup + steps, 2 * (warmup + steps))}
+    counts = (settle, warmup, steps, warmup, steps)
+    bounds, at = {}, 0
+    for ph, n in zip(PHASES, counts):
+        if n:
+            bounds[ph] = (at, at + n)
+        at += n
     out = {}
     for s, lst in durs.items():
-        if len(lst) != 2 * (warmup + steps):
-            raise ValueError(f"stage {s}: {len(lst)} dispatches, expected {2 * (warmup + steps)}")
+        if len(lst) != at:
+            raise ValueError(f"stage {s}: {len(lst)} dispatches, expected {at}")
         d = [v for _, v in sorted(lst)]
         out[s] = {ph: statistics.mean(d[a:b]) / 1e3 for ph, (a, b) in bounds.items()}
     return out
@@ -192,21 +203,85 @@ def trace(args) -> None:
         with open(args.bench_json) as fh:
             line = [l for l in fh if l.startswith("{")][-1]
         rec = json.loads(line)
+    summary = {"workload": args.workload, "direction": args.direction,
+               "command": f"rocprofv3 --kernel-trace --stats --output-format csv -d <dir> -o run -- "
+                          f"python3 bench.py {args.bench_args}", "kernels": {}}
+    for r in rows:
+        s = stage_of(r["Name"])
+        if s is not None:
+            summary["kernels"][KERNEL_NAMES[s]] = {"kernel_sha": kernel_sha(s), "calls": int(r["Calls"]),
+                                                   "average_us": float(r["AverageNs"]) / 1e3}
+    if args.phases == "auto" and rec is not None:
+        args.phases = f"{rec.get('settle_calls', 0)},{rec['warmup']},{rec['steps']}"
     if args.phases:
-        warmup, steps = (int(v) for v in args.phases.split(","))
-        pm = phase_means(args.stats, warmup, steps)
+        parts = [int(v) for v in args.phases.split(",")]
+        settle, warmup, steps = parts if len(parts) == 3 else [0] + parts
+        pm = phase_means(args.stats, warmup, steps, settle)
+        names = [ph for ph in PHASES if ph in pm[1]]
         md += ["", f"Mean duration per phase of the run (`run_kernel_trace.csv`, each stage's dispatches in start "
-               f"order: {warmup} warmup steps, {steps} timed eager steps, {warmup} + {steps} graph launches), in us:",
-               "", "| kernel | warmup | timed | graph warmup | graph | HIP events, timed steps |", "|---|---|---|---|---|---|"]
+               f"order: {settle} settle steps, {warmup} warmup steps, {steps} timed eager steps, {warmup} + {steps} "
+               f"graph launches), in us:",
+               "", "| kernel | " + " | ".join(names) + " | HIP events, timed steps |",
+               "|---|" + "---|" * len(names) + "---|"]
         for s in (1, 2, 3):
             ev = (rec or {}).get("per_stage_us", {}).get(KERNEL_NAMES[s])
-            md.append(f"| {KERNEL_NAMES[s]} | " + " | ".join(f"{pm[s][ph]:.1f}" for ph in
-                      ("warmup", "timed", "graph warmup", "graph")) + f" | {'' if ev is None else f'{ev:.1f}'} |")
+            md.append(f"| {KERNEL_NAMES[s]} | " + " | ".join(f"{pm[s][ph]:.1f}" for ph in names) +
+                      f" | {'' if ev is None else f'{ev:.1f}'} |")
+            summary["kernels"][KERNEL_NAMES[s]]["timed_us"] = pm[s]["timed"]
+            summary["kernels"][KERNEL_NAMES[s]]["phases_us"] = pm[s]
+            if ev is not None:
+                summary["kernels"][KERNEL_NAMES[s]]["hip_event_us"] = ev
     if rec is not None:
         md += ["", "The same process's own HIP-event timing of the timed steps (`per_stage_us` of its JSON line):",
                "", "```", json.dumps(rec.get("per_stage_us")), "```"]
     md.append("")
     with open(os.path.join(args.out, f"kernel_trace_{args.workload}_{args.direction}.md"), "w") as fh:
+        fh.write("\n".join(md))
+    with open(os.path.join(args.out, f"kernel_trace_{args.workload}_{args.direction}.json"), "w") as fh:
+        json.dump(summary, fh, indent=1)
+
+
+UTIL_COUNTERS = ("MfmaUtil", "VALUBusy", "MfmaFlopsBF16")
+
+
+def util(args) -> None:
+    """Matrix-core and vector-ALU utilisation per stage kernel from one
+    ``--pmc MfmaUtil VALUBusy MfmaFlopsBF16`` run (rocprofv3's derived
+    counters: MfmaUtil = 100 * sum SQ_VALU_MFMA_BUSY_CYCLES / (max
+    GRBM_GUI_ACTIVE * SIMD_NUM), VALUBusy = 100 * sum SQ_ACTIVE_INST_VALU /
+    CU_NUM / max GRBM_GUI_ACTIVE, MfmaFlopsBF16 = 512 * SQ_INSTS_VALU_MFMA_MOPS_BF16),
+    median over the dispatches of each kernel."""
+    from . import perf_model
+    import synthetic_inputs as si
+
+    wl = si.WORKLOADS[args.workload]
+    vals = {c: counter_per_dispatch(args.pmc, c) for c in UTIL_COUNTERS}
+    sf = perf_model.stage_flops(wl.B, wl.N, wl.c_z, wl.c)
+    cmd = (f"rocprofv3 --pmc {' '.join(UTIL_COUNTERS)} --output-format csv -d <dir> -o run -- "
+           f"python3 bench.py {args.bench_args}")
+    rec = {"workload": args.workload, "direction": args.direction, "command": cmd, "kernels": {}}
+    md = [f"# Matrix-core and vector-ALU utilisation: {args.workload}, {args.direction}", "",
+          "Command (from /tmp on the MI355X box, repository at $R):", "", "```",
+          cmd.replace("python3 bench.py", "python3 $R/bench.py"), "```", "",
+          "rocprofv3's derived counters, median over each kernel's dispatches: MfmaUtil = 100 * sum "
+          "SQ_VALU_MFMA_BUSY_CYCLES / (max GRBM_GUI_ACTIVE * SIMD_NUM); VALUBusy = 100 * sum "
+          "SQ_ACTIVE_INST_VALU / CU_NUM / max GRBM_GUI_ACTIVE; MfmaFlopsBF16 = 512 * "
+          "SQ_INSTS_VALU_MFMA_MOPS_BF16 (issued matrix-core flops, against the algorithmic flops).", "",
+          "| kernel | MfmaUtil (%) | VALUBusy (%) | MFMA flops issued (G) | algorithmic flops (G) |",
+          "|---|---|---|---|---|"]
+    for s in (1, 2, 3):
+        name = KERNEL_NAMES[s]
+        k = {c: _median_for(vals[c], lambda kn: stage_of(kn) == s) for c in UTIL_COUNTERS}
+        rec["kernels"][name] = {"kernel_sha": kernel_sha(s), "mfma_util_pct": k["MfmaUtil"],
+                                "valu_busy_pct": k["VALUBusy"], "mfma_flops_bf16": k["MfmaFlopsBF16"],
+                                "algorithmic_flops": sf[s - 1]}
+        md.append(f"| {name} | {k['MfmaUtil']:.1f} | {k['VALUBusy']:.1f} | {k['MfmaFlopsBF16'] / 1e9:.1f} | "
+                  f"{sf[s - 1] / 1e9:.1f} |")
+    md.append("")
+    base = os.path.join(args.out, f"util_{args.workload}_{args.direction}")
+    with open(base + ".json", "w") as fh:
+        json.dump(rec, fh, indent=1)
+    with open(base + ".md", "w") as fh:
         fh.write("\n".join(md))
 
 
@@ -222,10 +297,15 @@ def main() -> None:
         k.add_argument(a, required=True)
     k.add_argument("--bench-args", default="")
     k.add_argument("--bench-json", default=None, help="file holding the profiled run's JSON line")
-    k.add_argument("--phases", default=None, help="WARMUP,STEPS of the profiled bench.py run")
+    k.add_argument("--phases", default=None, help="[SETTLE,]WARMUP,STEPS of the profiled bench.py run, or 'auto' to read "
+                   "them from --bench-json")
+    u = sub.add_parser("util")
+    for a in ("--pmc", "--workload", "--direction", "--out"):
+        u.add_argument(a, required=True)
+    u.add_argument("--bench-args", default="")
     args = ap.parse_args()
     os.makedirs(args.out, exist_ok=True)
-    (traffic if args.cmd == "traffic" else trace)(args)
+    {"traffic": traffic, "trace": trace, "util": util}[args.cmd](args)
 
 
 if __name__ == "__main__":
