@@ -12,21 +12,20 @@
 // without a transpose. n_pad is a multiple of 64 and the padded columns hold
 // +0.0, so the k loop has no tail.
 //
-// Tile (default): 256 x 256 outputs per block of 8 waves (2 x 4), each wave
-// 128 (i) x 64 (j) as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks. K advances 64
-// columns per step through a 2-stage LDS ring filled by direct global->LDS
-// loads (global_load_lds_dwordx4), one step ahead of the matrix cores, one
-// barrier per step. The default launch is the persistent form
-// (k2_contract_p: one block per CU looping over its tiles, the next tile's
-// first fill overlapping the epilogue; other shapes: k2_config). The ring is
-// laid out in 256-byte lines (one line of the 64 four-byte banks) holding 4
-// rows of 32 k each, with the 16-byte chunk index XOR-ed by the line index,
-// so the 16 lanes of a fragment read hit 16 distinct bank groups. Rows past N are clamped to row N-1 (their results are
-// discarded). The epilogue stages the bf16 tile in LDS and writes 512-byte
+// Tile: 256 x 256 outputs per block of 8 waves (2 x 4), each wave 128 (i) x
+// 64 (j) as 4 x 2 v_mfma_f32_32x32x16_bf16 blocks. K advances 64 columns per
+// step through a 2-stage LDS ring filled by direct global->LDS loads
+// (global_load_lds_dwordx4), one step ahead of the matrix cores, one barrier
+// per step. This runs as a persistent kernel (k2_contract_p: one block per CU
+// looping over its tiles, the next tile's first fill overlapping the
+// epilogue). Up to N = 128, where 256 x 256 tiles are mostly padding, the
+// contraction runs on 128 x 128 tiles instead, one block each (k2_plan). The
+// ring is laid out in 256-byte lines (one line of the 64 four-byte banks)
+// holding 4 rows of 32 k each, with the 16-byte chunk index XOR-ed by the
+// line index, so the 16 lanes of a fragment read hit 16 distinct bank
+// groups. Rows past N are clamped to row N-1 (their results are discarded). The epilogue stages the bf16 tile in LDS and writes 512-byte
 // row segments of y. Blocks are numbered so that the tiles of one (channel,
 // batch) matrix run on one XCD and share its L2.
-
-#include <cstdlib>
 
 #include "trimul_device.hpp"
 #include "trimul_kernels.hpp"
@@ -411,33 +410,11 @@ __global__ __launch_bounds__(K2_THREADS) void k2_contract_p(const K2Args p) {
   }
 }
 
-// explicit instantiations of every configuration's kernel (and its host stub)
-template __global__ void k2_contract<256, 256, 32, 4, 2, 4>(const K2Args);
-template __global__ void k2_contract<256, 128, 64, 3, 4, 2>(const K2Args);
-template __global__ void k2_contract<256, 256, 64, 2, 2, 4>(const K2Args);
-template __global__ void k2_contract<128, 256, 64, 3, 2, 4>(const K2Args);
+// the small-N tile: 128 x 128, k 64, three stages, 8 waves of 64 x 32
+using CfgSmall = K2Cfg<128, 128, 64, 3, 2, 4>;
+template __global__ void k2_contract<128, 128, 64, 3, 2, 4>(const K2Args);
 
 namespace {
-
-// The tile configurations (see k2_config below).
-using CfgSq32 = K2Cfg<256, 256, 32, 4, 2, 4>;   // 256 x 256, k 32, 4 stages
-using CfgRect64 = K2Cfg<256, 128, 64, 3, 4, 2>; // 256 x 128, k 64, 3 stages
-using CfgSq64 = K2Cfg<256, 256, 64, 2, 2, 4>;   // 256 x 256, k 64, 2 stages
-using CfgTall64 = K2Cfg<128, 256, 64, 3, 2, 4>; // 128 x 256, k 64, 3 stages
-
-// 0: 256 x 256 k 32, 4 stages; 1: 256 x 128 k 64, 3 stages; 2 (default):
-// 256 x 256 k 64, 2 stages, persistent; 3: 128 x 256 k 64, 3 stages;
-// 4: configuration 2 without the persistent loop
-int k2_config() {
-  // read once per process (a function-local static: initialised exactly once
-  // even when several host threads make the first call together)
-  static const int cfg = [] {
-    int c = 2;
-    if (const char* e = std::getenv("TRIMUL_K2_TILE")) c = std::atoi(e);
-    return (c >= 0 && c <= 4) ? c : 2;
-  }();
-  return cfg;
-}
 
 template <class C>
 void tiles_of(int N, int& tm, int& tn) {
@@ -447,34 +424,41 @@ void tiles_of(int N, int& tm, int& tn) {
 
 }  // namespace
 
-void k2_tiles(int N, int& tiles_m, int& tiles_n) {
-  switch (k2_config()) {
-    case 0: tiles_of<CfgSq32>(N, tiles_m, tiles_n); break;
-    case 3: tiles_of<CfgTall64>(N, tiles_m, tiles_n); break;
-    case 1: tiles_of<CfgRect64>(N, tiles_m, tiles_n); break;
-    default: tiles_of<CfgSq64>(N, tiles_m, tiles_n); break;   // 2 and 4
+// The contraction's tile for one call (page "Triangle Multiplicative Update
+// (SM100 / SM103 / SM107)", section "Overview": the contraction is compiled
+// for a tile chosen per N from measured runs). 256 x 256 persistent tiles
+// read the fewest operand bytes per flop. Up to N = 128 they are mostly
+// padding (at N = 64 a quarter of each tile's rows and columns are real
+// pairs), and 128 x 128 tiles are faster: measured on the MI355X, 6.7 vs 9.0
+// us at N = 64, 8.4 vs 11.7 us at N = 128 (c = 128), 9.1 vs 12.0 us at N =
+// 128, c = 256. From N = 129 on the two are level or the large tile is faster
+// (N = 192 and 256 at c = 128: 12.5 / 12.5 and 14.3 / 14.6 us, although the
+// large tiles then leave half the CUs idle; N = 384: 34.3 / 33.2 us; c = 256,
+// N = 192: 20.3 / 14.8 us).
+void k2_plan(K2Args& a) {
+  int tm, tn;
+  tiles_of<CfgP>(a.N, tm, tn);
+  if (a.n_pad <= CfgSmall::BM) {
+    a.tile = K2_TILE_128;
+    tiles_of<CfgSmall>(a.N, a.tiles_m, a.tiles_n);
+  } else {
+    a.tile = K2_TILE_256P;
+    a.tiles_m = tm;
+    a.tiles_n = tn;
   }
-}
-
-template <class C>
-void launch_cfg(const K2Args& a, hipStream_t stream) {
-  hipLaunchKernelGGL((k2_contract<C::BM, C::BN, C::BK, C::STAGES, C::WM, C::WN>), dim3(a.nblocks),
-                     dim3(K2_THREADS), 0, stream, a);
+  a.nblocks = a.tiles_m * a.tiles_n * a.c * a.B;
 }
 
 hipError_t launch_k2(const K2Args& a, int max_blocks, hipStream_t stream) {
-  switch (k2_config()) {
-    case 0: launch_cfg<CfgSq32>(a, stream); break;
-    case 3: launch_cfg<CfgTall64>(a, stream); break;
-    case 1: launch_cfg<CfgRect64>(a, stream); break;
-    case 4: launch_cfg<CfgSq64>(a, stream); break;
-    default: {
-      // one persistent block per CU, a multiple of 8 (one share per XCD) when possible
-      int grid = a.nblocks < max_blocks ? a.nblocks : max_blocks;
-      if (grid > 8) grid &= ~7;
-      hipLaunchKernelGGL(k2_contract_p, dim3(grid), dim3(K2_THREADS), 0, stream, a);
-      break;
-    }
+  if (a.tile == K2_TILE_128) {
+    hipLaunchKernelGGL((k2_contract<CfgSmall::BM, CfgSmall::BN, CfgSmall::BK, CfgSmall::STAGES, CfgSmall::WM,
+                                    CfgSmall::WN>),
+                       dim3(a.nblocks), dim3(K2_THREADS), 0, stream, a);
+  } else {
+    // one persistent block per CU, a multiple of 8 (one share per XCD) when possible
+    int grid = a.nblocks < max_blocks ? a.nblocks : max_blocks;
+    if (grid > 8) grid &= ~7;
+    hipLaunchKernelGGL(k2_contract_p, dim3(grid), dim3(K2_THREADS), 0, stream, a);
   }
   return hipGetLastError();
 }

@@ -242,8 +242,7 @@ int run(int first_stage, int last_stage, const void* x, const void* mask, const 
       a.N = N;
       a.n_pad = n_pad;
       a.c = c;
-      trimul::k2_tiles(N, a.tiles_m, a.tiles_n);
-      a.nblocks = a.tiles_m * a.tiles_n * c * B;
+      trimul::k2_plan(a);
       e = trimul::launch_k2(a, info.cus, s);
     } else {
       trimul::K3Args a;

@@ -50,13 +50,16 @@ struct K1Args {
 };
 
 // Stage 2: per-channel contraction y(ch, r, j) = sum_k a(ch, r, k) b(ch, r', k).
+constexpr int K2_TILE_256P = 0;   // 256 x 256 tiles, persistent blocks
+constexpr int K2_TILE_128 = 1;    // 128 x 128 tiles, one block per tile
 struct K2Args {
   const uint16_t* plane_a;
   const uint16_t* plane_b;
   uint16_t* plane_y;
   int B, N, n_pad, c;
+  int tile;                 // K2_TILE_*, chosen by k2_plan
   int tiles_m, tiles_n;     // output tiles per (channel, batch) matrix
-  int nblocks;
+  int nblocks;              // tiles in all
 };
 
 // Stage 3: LayerNorm_out + LayerNorm_in recomputed + gated output projection.
@@ -85,6 +88,7 @@ hipError_t launch_k3(const K3Args& a, int grid_x, hipStream_t stream);
 
 int k1_tiles(int B, int N);
 int k3_tiles(int B, int N);
-void k2_tiles(int N, int& tiles_m, int& tiles_n);
+// the contraction's tile for the shape set in a (tile, tiles_m, tiles_n, nblocks)
+void k2_plan(K2Args& a);
 
 }  // namespace trimul
