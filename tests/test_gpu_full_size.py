@@ -71,3 +71,32 @@ def test_full_size_every_cell(gpu, name, direction):
         closed = T.output(z, u, prm)
         assert_within_tolerance(out_h[0][pad].astype(np.float64), closed,
                                 f"{name} {direction} padded pairs (closed form)")
+
+
+def test_maximum_extent_sampled(gpu):
+    """The largest problem the 32-bit extent rule serves at c = 256 and B = 1:
+    N = 2040, 2 * c * B * N * n_pad = 2 139 095 040 < 2^31 (N = 2048 is declined).
+    The oracle runs on sampled output blocks (every row block of 64 pairs and the
+    ragged last one, against columns across the 256-wide contraction tiles and
+    the last column), every cell of those blocks held to the bar; the whole
+    output is checked finite."""
+    from triangle_multiplicative_update_amd import check_support
+    N, c = 2040, 256
+    check_support(1, N, c, c, "outgoing")
+    with pytest.raises(NotImplementedError):
+        check_support(1, 2048, c, c, "outgoing")
+    wl = si.custom(1, N, c, mask="bernoulli", seed=2040)
+    inp = si.generate(wl)
+    say(f"[gpu] maximum extent N={N} c={c} outgoing")
+    d = to_device(inp, gpu)
+    with torch.no_grad():
+        out = call(d, "outgoing")
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(out).all())
+    rows = [0, 63, 64, 255, 256, 1023, 1024, 1983, 1984, 2039]
+    cols = [0, 1, 255, 256, 511, 512, 1279, 1280, 2038, 2039]
+    got = out[0][rows][:, cols].float().cpu().numpy().astype(np.float64)
+    del out, d
+    torch.cuda.empty_cache()
+    _, ref = oracle.forward_block(inp, "outgoing", rows, cols)
+    assert_within_tolerance(got, ref, f"N={N} c={c} sampled blocks", sampled=True)

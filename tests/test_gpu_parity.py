@@ -47,6 +47,7 @@ CASES = [
     (1, 1, 128, "ones", True),
     (2, 136, 256, "bernoulli", True),
     (1, 45, 256, "padded", False),
+    (2, 100, 256, "bernoulli", True),    # 128 x 128 contraction tiles, 512 matrices
     (3, 24, 128, "none", True),
     # several stage-2 tiles per persistent block, the last one ragged
     (1, 300, 128, "padded", True),
