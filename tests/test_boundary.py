@@ -210,3 +210,27 @@ def test_plan_declines_without_gpu():
         api.prepare_weights(w, w, None, None, m, None, w, w, o, None, o, None)
     with pytest.raises(NotImplementedError, match="precision"):
         api.prepare_weights(w, w, m, None, m, None, w, w, o, None, o, None, precision="tf32")
+
+
+def test_drop_in_signature_pin():
+    """The drop-in function's parameters: the page's names, order and defaults
+    (section "Drop-in function"), out= and stream= keyword-only."""
+    import inspect
+    sig = inspect.signature(api.triangle_multiplicative_update)
+    names = list(sig.parameters)
+    assert names[:17] == ["x", "direction", "mask", "norm_in_weight", "norm_in_bias", "p_in_weight",
+                          "p_in_bias", "g_in_weight", "g_in_bias", "norm_out_weight", "norm_out_bias",
+                          "p_out_weight", "p_out_bias", "g_out_weight", "g_out_bias", "eps", "precision"]
+    p = sig.parameters
+    assert p["direction"].default == "outgoing" and p["eps"].default == 1e-5
+    assert p["precision"].default is None
+    assert all(p[n].default is None for n in names[2:15])
+    for n in ("out", "stream"):
+        assert p[n].kind is inspect.Parameter.KEYWORD_ONLY and p[n].default is None
+    # the prepared class API (section "Prepared class API")
+    pw = list(inspect.signature(api.prepare_weights).parameters)
+    assert pw == names[3:15] + ["precision"]
+    fwd = list(inspect.signature(api.TriangleMultiplicativeUpdateFwd.__init__).parameters)
+    assert fwd[1:7] == ["x", "direction", "c_hidden", "has_mask", "has_in_bias", "has_out_bias"]
+    ex = list(inspect.signature(api.TriangleMultiplicativeUpdateFwd.execute).parameters)
+    assert ex[1:6] == ["x", "mask", "weights", "out", "workspace"]

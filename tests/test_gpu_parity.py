@@ -86,3 +86,53 @@ def test_fractional_mask(gpu, direction):
     inp = dict(inp)
     inp["mask"] = (m.view(np.uint32) >> 16).astype(np.uint16)   # exact: truncation, then used as given
     _run_and_check(inp, direction, "b1_n96_c128_fractional", gpu)
+
+
+# A seeded sweep of shapes the fixed cases do not name: every combination is
+# drawn once from a fixed generator (N from 1 to 320 across the 64-pair and
+# 128 / 256 contraction tile edges, B up to 3, both widths, every mask kind,
+# biases on or off, both directions).
+def _sweep_cases(n=16, seed=20261202):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for _ in range(n):
+        c = int(rng.choice([128, 256]))
+        B = int(rng.integers(1, 4)) if c == 128 else int(rng.integers(1, 3))
+        N = int(rng.integers(1, 321)) if c == 128 else int(rng.integers(1, 200))
+        mask = str(rng.choice(["none", "ones", "bernoulli", "padded"]))
+        biases = bool(rng.integers(0, 2))
+        direction = str(rng.choice(["outgoing", "incoming"]))
+        cases.append((B, N, c, mask, biases, direction, int(rng.integers(0, 1 << 30))))
+    return cases
+
+
+@pytest.mark.parametrize("B,N,c,mask,biases,direction,seed", _sweep_cases())
+def test_parity_sweep(gpu, B, N, c, mask, biases, direction, seed):
+    wl = si.custom(B, N, c, mask=mask, mask_p=0.8, mask_len=max(1, (2 * N) // 3), biases=biases,
+                   seed=seed)
+    _run_and_check(si.generate(wl), direction, wl.name, gpu)
+
+
+def test_two_streams_at_once(gpu):
+    """Two calls in flight on two streams at once (separate outputs and
+    workspaces) give the bits each gives alone."""
+    from triangle_multiplicative_update_amd import triangle_multiplicative_update as tmu
+    d1 = to_device(si.generate(si.custom(1, 200, 128, mask="bernoulli", seed=71)), gpu)
+    d2 = to_device(si.generate(si.custom(2, 96, 256, mask="padded", mask_len=80, seed=72)), gpu)
+    say("[gpu] two streams at once")
+    with torch.no_grad():
+        r1 = call(d1, "outgoing")
+        r2 = call(d2, "incoming")
+        torch.cuda.synchronize()
+        s1, s2 = torch.cuda.Stream(gpu), torch.cuda.Stream(gpu)
+        outs = []
+        for rep in range(3):
+            o1 = tmu(d1["x"], "outgoing", d1["mask"], *[d1[k] for k in si.PARAM_NAMES], stream=s1)
+            o2 = tmu(d2["x"], "incoming", d2["mask"], *[d2[k] for k in si.PARAM_NAMES], stream=s2)
+            outs.append((o1, o2))
+        torch.cuda.current_stream(gpu).wait_stream(s1)
+        torch.cuda.current_stream(gpu).wait_stream(s2)
+    torch.cuda.synchronize()
+    for o1, o2 in outs:
+        assert torch.equal(o1.view(torch.int16), r1.view(torch.int16))
+        assert torch.equal(o2.view(torch.int16), r2.view(torch.int16))
