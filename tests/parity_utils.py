@@ -1,9 +1,9 @@
 """Helpers shared by the GPU parity tests: device upload, the call through the
 C ABI, reading the workspace planes, and the acceptance statistics.
 
-Acceptance bar for the output (spec tolerance of the operation, in line
-with the page "Triangle Multiplicative Update (SM100 / SM103 / SM107)", section
-"Mathematics and numerics", measured numerics):
+Acceptance bar for the output (the tolerance this library holds itself to, in
+line with the page "Triangle Multiplicative Update (SM100 / SM103 / SM107)",
+section "Mathematics and numerics", measured numerics):
   * relative RMS  ||gpu - ref||_2 / ||ref||_2  <= 2e-3
   * |gpu - ref| <= 4e-3 + |ref|/64 on all but 10 per million cells
   * |gpu - ref| <= 2e-2 + |ref|/64 on every cell
