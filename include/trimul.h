@@ -152,8 +152,10 @@ int trimul_forward_stage(int stage,
  * declined with TRIMUL_E_UNSUPPORTED before any launch (c = 128, B = 1 is
  * served up to N = 273; c = 256, B = 1 up to N = 192); use trimul_forward then.
  * No allocation and no synchronization happen on any call; the first call on
- * a device also looks up that device's copy of the array (not a stream
- * operation). The array keeps the last call's planes; no part of it needs to
+ * a device also reads the device's properties and looks up that device's copy
+ * of the array (neither is a stream operation, but a capture that forbids
+ * such calls would refuse them: make the first call on each device outside
+ * any stream capture). The array keeps the last call's planes; no part of it needs to
  * start at zero. Every call on one GPU shares that GPU's array: calls that
  * overlap in time on one GPU (different streams or host threads without
  * ordering between them) race and give undefined results. */

@@ -23,9 +23,10 @@
 // ring is laid out in 256-byte lines (one line of the 64 four-byte banks)
 // holding 4 rows of 32 k each, with the 16-byte chunk index XOR-ed by the
 // line index, so the 16 lanes of a fragment read hit 16 distinct bank
-// groups. Rows past N are clamped to row N-1 (their results are discarded). The epilogue stages the bf16 tile in LDS and writes 512-byte
-// row segments of y. Blocks are numbered so that the tiles of one (channel,
-// batch) matrix run on one XCD and share its L2.
+// groups. Rows past N are clamped to row N-1 (their results are discarded).
+// The epilogue stages the bf16 tile in LDS and writes 512-byte row segments
+// of y. Blocks are numbered so that the tiles of one (channel, batch) matrix
+// run on one XCD and share its L2.
 
 #include "trimul_device.hpp"
 #include "trimul_kernels.hpp"
@@ -429,12 +430,12 @@ void tiles_of(int N, int& tm, int& tn) {
 // for a tile chosen per N from measured runs). 256 x 256 persistent tiles
 // read the fewest operand bytes per flop. Up to N = 128 they are mostly
 // padding (at N = 64 a quarter of each tile's rows and columns are real
-// pairs), and 128 x 128 tiles are faster: measured on the MI355X, 6.7 vs 9.0
-// us at N = 64, 8.4 vs 11.7 us at N = 128 (c = 128), 9.1 vs 12.0 us at N =
-// 128, c = 256. From N = 129 on the two are level or the large tile is faster
-// (N = 192 and 256 at c = 128: 12.5 / 12.5 and 14.3 / 14.6 us, although the
-// large tiles then leave half the CUs idle; N = 384: 34.3 / 33.2 us; c = 256,
-// N = 192: 20.3 / 14.8 us).
+// pairs), and 128 x 128 tiles are faster: measured on the MI355X (128 x 128
+// against 256 x 256), 6.7 vs 9.0 us at N = 64, 8.4 vs 11.7 us at N = 128 (c =
+// 128), 9.1 vs 12.0 us at N = 128, c = 256. From N = 129 on the two are level
+// or the large tile is faster: 12.5 vs 12.5 us at N = 192 and 14.3 vs 14.6 us
+// at N = 256 (c = 128, although the large tiles then leave half the CUs idle),
+// 34.3 vs 33.2 us at N = 384, 20.3 vs 14.8 us at N = 192, c = 256.
 void k2_plan(K2Args& a) {
   int tm, tn;
   tiles_of<CfgP>(a.N, tm, tn);
