@@ -37,6 +37,12 @@ def test_workload_n256_incoming_bernoulli(gpu):
     _run_and_check(inp, "incoming", "n256_c128_bern", gpu)
 
 
+def test_small_workloads_other_direction(gpu):
+    # the N = 64 and N = 256 workloads in the direction their workload does not list
+    _run_and_check(workload_inputs("n64_c128_ones"), "incoming", "n64_c128_ones", gpu)
+    _run_and_check(workload_inputs("n256_c128_bern"), "outgoing", "n256_c128_bern", gpu)
+
+
 CASES = [
     # (B, N, c, mask, biases)  -- ragged tails against the 64-pair and 128x128 tiles
     (1, 200, 128, "bernoulli", True),
