@@ -9,10 +9,11 @@ per extra distinct address on the busiest bank.
 
 Each address function below restates, in Python, the index arithmetic of the
 C++ function or expression it names, so that a change to a layout there has
-to be mirrored here and re-checked. The stage-2 ring and the stage-3 tiles
-(including the c = 256 form's direct-load staging) are conflict-free; stage 1's padded z and staging tiles cost 384 extra cycles per
-tile, the count SQ_LDS_BANK_CONFLICT reads for that kernel (13.8 K per CU over
-36 tiles at N = 768).
+to be mirrored here and re-checked. The stage-2 ring, the stage-3 tiles
+(including the c = 256 form's direct-load staging) and the c_z = 256 stage-1
+pair tile are conflict-free; the c_z = 128 stage 1's padded z and staging
+tiles cost 384 extra cycles per tile, the count SQ_LDS_BANK_CONFLICT reads for
+that kernel (13.8 K per CU over 36 tiles at N = 768).
 """
 
 import pytest
@@ -195,3 +196,56 @@ def test_stage1_padded_tiles_cost_what_the_counter_reads():
         for ks in range(8):
             assert extra_cycles([((32 * mb + (l & 31)) * ZP + 16 * ks + 8 * (l >> 5)) * 2 for l in range(64)], 16) == 0
     assert extra == 384
+
+
+# ---- stage 1, c_z = 256: the pair-tile ring of k1_ln_proj_wide ----
+def wide_swz(r):
+    return ((r & 1) << 1) | ((((r >> 1) ^ (r >> 3)) & 1) << 2) | (((r >> 1) & 1) << 3)
+
+
+def wide_pos(r, c):
+    """byte offset of 16-byte chunk c of pair row r (512-byte rows)"""
+    return r * 512 + ((c ^ wide_swz(r)) << 4)
+
+
+def test_stage1_wide_tile_is_conflict_free_and_complete():
+    # direct loads: load q of wave w fills slots (4w + q) * 64 + lane with chunk
+    # (lane % 32) ^ wide_swz(row) of row 8w + 2q + lane / 32; every (row, chunk)
+    # lands exactly once, at wide_pos
+    seen = set()
+    for w in range(8):
+        x0 = [((l & 31) ^ wide_swz(8 * w + (l >> 5))) << 4 for l in range(64)]
+        x1 = [((l & 31) ^ wide_swz(8 * w + 2 + (l >> 5))) << 4 for l in range(64)]
+        for q in range(4):
+            for l in range(64):
+                s = (4 * w + q) * 64 + l
+                pr = 8 * w + 2 * q + (l >> 5)
+                c = ((x1 if q & 1 else x0)[l]) >> 4
+                assert wide_pos(pr, c) == 16 * s
+                seen.add((pr, c))
+    assert len(seen) == 64 * 32
+    # LayerNorm rows (reads and in-place writes, 16 bytes): pair 8w + l / 8,
+    # chunk l % 8 + 8 c, through the two lane offsets of the kernel
+    for w in range(8):
+        for c in range(4):
+            addr = []
+            for l in range(64):
+                lp, sub = 8 * w + (l >> 3), l & 7
+                s = wide_swz(lp)
+                lrow0 = lp * 512 + (((sub ^ (s & 7)) + 8 * ((s >> 3) & 1)) << 4)
+                a = (lrow0 ^ 128 if c & 1 else lrow0) + 256 * (c >> 1)
+                assert a == wide_pos(lp, sub + 8 * c)
+                addr.append(a)
+            assert extra_cycles(addr, 16) == 0
+    # A-fragment reads of the 16 x 16 x 32 MFMAs: row 16 pg + l % 16, chunk
+    # 4 ks + l / 16, through the four lane offsets of the kernel
+    for pg in range(4):
+        for ks in range(8):
+            addr = []
+            for l in range(64):
+                l16, q4 = l & 15, l >> 4
+                aoff = l16 * 512 + (((4 * (ks & 3) + q4) ^ wide_swz(l16)) << 4)
+                a = aoff + 256 * (ks >> 2) + 8192 * pg
+                assert a == wide_pos(16 * pg + l16, 4 * ks + q4)
+                addr.append(a)
+            assert extra_cycles(addr, 16) == 0

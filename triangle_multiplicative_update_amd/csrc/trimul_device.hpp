@@ -54,6 +54,11 @@ __device__ __forceinline__ u32x4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_
 __device__ __forceinline__ void buffer_store16(__amdgpu_buffer_rsrc_t r, const u32x4& v, uint32_t voff) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, voff, 0, 0);
 }
+// 8-byte buffer store at byte offset voff (8 bytes are read in one cycle, so
+// the data registers are free for the next instruction)
+__device__ __forceinline__ void buffer_store8(__amdgpu_buffer_rsrc_t r, const u32x2& v, uint32_t voff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, 0, 0);
+}
 __device__ __forceinline__ bf16x8 ld_frag(const void* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 typedef __attribute__((address_space(3))) void lds_void;
@@ -64,6 +69,26 @@ typedef __attribute__((address_space(3))) void lds_void;
 __device__ __forceinline__ void load_lds16(const void* g, void* lds) {
   __builtin_amdgcn_global_load_lds(g, (lds_void*)lds, 16, 0, 0);
 }
+
+// The same copy issued as inline assembly, from a uniform base `gbase` plus
+// a per-lane 32-bit byte offset. The compiler's wait-count model treats a
+// direct load like a flat access that may retire out of order, and while one
+// is in flight it waits for zero outstanding operations before every LDS
+// read and every use of a loaded register; issued this way the copy is
+// invisible to that model, so the compiler's own waits stay exact (an extra
+// operation in the counters only makes them wait longer). The caller waits
+// for the copy itself with wait_vm. Only for kernels in which no other code
+// uses M0 (the LDS address register of the copy).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16_asm(const void* gbase, uint32_t voff, const void* lds) {
+  const uint32_t lds_addr = uint32_t(reinterpret_cast<uintptr_t>(lds));
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(gbase)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // wait until at most n vector-memory operations of this wave are outstanding
 // (they retire in issue order)
@@ -155,57 +180,135 @@ __device__ __forceinline__ int lds_swz(int r) {
 // Rows of 4 or more chunks per lane (c_z = 256) unpack the bf16 input again
 // in each pass instead of keeping 8 * NV floats live across the two
 // reductions; the values, and so the result bits, are the same either way.
-template <int NV, class WB>
-__device__ __forceinline__ void layer_norm_row_wb(const u32x4 (&xin)[NV], WB&& affine, float eps,
-                                                  u32x4 (&zout)[NV]) {
+// Those rows go through the three passes below, which a kernel may also call
+// one at a time (with the row re-read in between): the same operations in the
+// same order, so the same bits.
+
+// The passes are also available one 16-byte chunk at a time (c = 0, 1, ...
+// in order), for kernels that spread a row's LayerNorm over other work.
+// pass 1: partial sums of chunk c (element i = 8 c + e into sum i % 4)
+__device__ __forceinline__ void ln_sum_chunk(float (&sp)[4], const u32x4& x, int c) {
+#pragma clang fp contract(off)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int i = 8 * c + e;
+    const float v = (e & 1) ? bf16_hi(x[e >> 1]) : bf16_lo(x[e >> 1]);
+    sp[i & 3] = (i < 4) ? v : sp[i & 3] + v;
+  }
+}
+// the row mean from the partial sums (every lane of the 8 ends with the same bits)
+template <int NV>
+__device__ __forceinline__ float ln_mean_of(const float (&sp)[4]) {
 #pragma clang fp contract(off)
   constexpr float inv_n = 1.0f / float(64 * NV);
-  constexpr bool kKeep = NV <= 2;
-  float v[kKeep ? NV : 1][8];
-  auto elem = [&](int c, int e) -> float {
-    if constexpr (kKeep) return v[c][e];
-    else return (e & 1) ? bf16_hi(xin[c][e >> 1]) : bf16_lo(xin[c][e >> 1]);
-  };
-  if constexpr (kKeep) {
+  return sum_lanes8((sp[0] + sp[1]) + (sp[2] + sp[3])) * inv_n;
+}
+// pass 2: partial sums of squared deviations of chunk c
+__device__ __forceinline__ void ln_sq_chunk(float (&ssp)[4], const u32x4& x, int c, float mean) {
+#pragma clang fp contract(off)
 #pragma unroll
-    for (int c = 0; c < NV; ++c) unpack8(xin[c], v[c]);
+  for (int e = 0; e < 8; ++e) {
+    const int i = 8 * c + e;
+    const float d = ((e & 1) ? bf16_hi(x[e >> 1]) : bf16_lo(x[e >> 1])) - mean;
+    ssp[i & 3] = (i < 4) ? d * d : __builtin_fmaf(d, d, ssp[i & 3]);
   }
-  // in-lane sums as four interleaved partial sums (element i into sum i % 4),
-  // combined pairwise: dependency chains of 4 + 2 instead of 16, which a
-  // single wave per SIMD can issue without stalling
+}
+// 1 / sqrt(biased variance + eps) from the partial sums
+template <int NV>
+__device__ __forceinline__ float ln_rstd_of(const float (&ssp)[4], float eps) {
+#pragma clang fp contract(off)
+  constexpr float inv_n = 1.0f / float(64 * NV);
+  const float var = sum_lanes8((ssp[0] + ssp[1]) + (ssp[2] + ssp[3])) * inv_n;
+  return __builtin_amdgcn_rsqf(var + eps);
+}
+// pass 3 on one chunk: normalise, affine, round to bf16
+__device__ __forceinline__ u32x4 ln_apply_chunk(const u32x4& x, float mean, float rstd, const float (&wv)[8],
+                                                const float (&bv)[8]) {
+#pragma clang fp contract(off)
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float v = (e & 1) ? bf16_hi(x[e >> 1]) : bf16_lo(x[e >> 1]);
+    o[e] = __builtin_fmaf((v - mean) * rstd, wv[e], bv[e]);
+  }
+  return u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]), pack_bf16x2(o[6], o[7])};
+}
+
+// the three passes over a whole row held by the lane
+template <int NV>
+__device__ __forceinline__ float ln_mean(const u32x4 (&x)[NV]) {
   float sp[4];
 #pragma unroll
-  for (int c = 0; c < NV; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int i = 8 * c + e;
-      sp[i & 3] = (i < 4) ? elem(c, e) : sp[i & 3] + elem(c, e);
-    }
-  float s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-  s = sum_lanes8(s);
-  const float mean = s * inv_n;
+  for (int c = 0; c < NV; ++c) ln_sum_chunk(sp, x[c], c);
+  return ln_mean_of<NV>(sp);
+}
+template <int NV>
+__device__ __forceinline__ float ln_rstd(const u32x4 (&x)[NV], float mean, float eps) {
   float ssp[4];
 #pragma unroll
-  for (int c = 0; c < NV; ++c)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int i = 8 * c + e;
-      const float d = elem(c, e) - mean;
-      ssp[i & 3] = (i < 4) ? d * d : __builtin_fmaf(d, d, ssp[i & 3]);
-    }
-  float ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);
-  ss = sum_lanes8(ss);
-  const float var = ss * inv_n;
-  const float rstd = __builtin_amdgcn_rsqf(var + eps);
+  for (int c = 0; c < NV; ++c) ln_sq_chunk(ssp, x[c], c, mean);
+  return ln_rstd_of<NV>(ssp, eps);
+}
+template <int NV, class WB>
+__device__ __forceinline__ void ln_apply(const u32x4 (&x)[NV], float mean, float rstd, WB&& affine,
+                                         u32x4 (&z)[NV]) {
 #pragma unroll
   for (int c = 0; c < NV; ++c) {
     float wv[8], bv[8];
     affine(c, wv, bv);
-    float o[8];
+    z[c] = ln_apply_chunk(x[c], mean, rstd, wv, bv);
+  }
+}
+
+template <int NV, class WB>
+__device__ __forceinline__ void layer_norm_row_wb(const u32x4 (&xin)[NV], WB&& affine, float eps,
+                                                  u32x4 (&zout)[NV]) {
+#pragma clang fp contract(off)
+  if constexpr (NV > 2) {
+    const float mean = ln_mean<NV>(xin);
+    ln_apply<NV>(xin, mean, ln_rstd<NV>(xin, mean, eps), affine, zout);
+  } else {
+    constexpr float inv_n = 1.0f / float(64 * NV);
+    float v[NV][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf((elem(c, e) - mean) * rstd, wv[e], bv[e]);
-    zout[c] = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                    pack_bf16x2(o[6], o[7])};
+    for (int c = 0; c < NV; ++c) unpack8(xin[c], v[c]);
+    // in-lane sums as four interleaved partial sums (element i into sum i % 4),
+    // combined pairwise: dependency chains of 4 + 2 instead of 16, which a
+    // single wave per SIMD can issue without stalling
+    float sp[4];
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * c + e;
+        sp[i & 3] = (i < 4) ? v[c][e] : sp[i & 3] + v[c][e];
+      }
+    float s = (sp[0] + sp[1]) + (sp[2] + sp[3]);
+    s = sum_lanes8(s);
+    const float mean = s * inv_n;
+    float ssp[4];
+#pragma unroll
+    for (int c = 0; c < NV; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * c + e;
+        const float d = v[c][e] - mean;
+        ssp[i & 3] = (i < 4) ? d * d : __builtin_fmaf(d, d, ssp[i & 3]);
+      }
+    float ss = (ssp[0] + ssp[1]) + (ssp[2] + ssp[3]);
+    ss = sum_lanes8(ss);
+    const float var = ss * inv_n;
+    const float rstd = __builtin_amdgcn_rsqf(var + eps);
+#pragma unroll
+    for (int c = 0; c < NV; ++c) {
+      float wv[8], bv[8];
+      affine(c, wv, bv);
+      float o[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf((v[c][e] - mean) * rstd, wv[e], bv[e]);
+      zout[c] = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                      pack_bf16x2(o[6], o[7])};
+    }
   }
 }
 
@@ -376,6 +479,13 @@ __device__ __forceinline__ float gate_masked(float g, float v, float mb, float m
 
 __device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// D (16 x 16) += A (16 x 32) B (32 x 16): lane l supplies row l % 16 of A and
+// column l % 16 of B, each at k = 8 (l / 16) .. + 7, and receives
+// D[4 (l / 16) + i][l % 16] in register i
+__device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
 }  // namespace trimul
