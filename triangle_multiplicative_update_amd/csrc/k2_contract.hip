@@ -104,33 +104,30 @@ __global__ __launch_bounds__(K2_THREADS) void k2_contract(const K2Args p) {
   const int N = p.N, ld = p.n_pad;
   const int i0 = tm * C::BM, j0 = tn * C::BN;
   const size_t base = size_t(mat) * N * ld;
-  const uint16_t* Ag = p.plane_a + base;
-  const uint16_t* Bg = p.plane_b + base;
 
-  // this lane's load sources (rows past N clamp to N - 1)
-  const uint16_t* srcA[C::IA];
-  const uint16_t* srcB[C::IB];
+  // this lane's load sources as byte offsets into the planes (every plane is
+  // below 2^31 bytes); rows past N clamp to N - 1
+  uint32_t srcA[C::IA], srcB[C::IB];
 #pragma unroll
   for (int t = 0; t < C::IA; ++t) {
     int r, c;
     C::src((wave * C::IA + t) * 64 + lane, r, c);
-    srcA[t] = Ag + size_t(min(i0 + r, N - 1)) * ld + 8 * c;
+    srcA[t] = uint32_t((base + size_t(min(i0 + r, N - 1)) * ld + 8 * c) * 2);
   }
 #pragma unroll
   for (int t = 0; t < C::IB; ++t) {
     int r, c;
     C::src((wave * C::IB + t) * 64 + lane, r, c);
-    srcB[t] = Bg + size_t(min(j0 + r, N - 1)) * ld + 8 * c;
+    srcB[t] = uint32_t((base + size_t(min(j0 + r, N - 1)) * ld + 8 * c) * 2);
   }
   auto issue = [&](int step) {
     uint8_t* st = smem + (step % C::STAGES) * C::STAGE_BYTES;
-    const int k0 = step * C::BK;
+    const uint16_t* ga = p.plane_a + step * C::BK;
+    const uint16_t* gb = p.plane_b + step * C::BK;
 #pragma unroll
-    for (int t = 0; t < C::IA; ++t)
-      load_lds16(srcA[t] + k0, st + (wave * C::IA + t) * 1024);
+    for (int t = 0; t < C::IA; ++t) load_lds16_asm(ga, srcA[t], st + (wave * C::IA + t) * 1024);
 #pragma unroll
-    for (int t = 0; t < C::IB; ++t)
-      load_lds16(srcB[t] + k0, st + C::A_BYTES + (wave * C::IB + t) * 1024);
+    for (int t = 0; t < C::IB; ++t) load_lds16_asm(gb, srcB[t], st + C::A_BYTES + (wave * C::IB + t) * 1024);
   };
 
   constexpr int SUB = C::BK / 16;
@@ -169,19 +166,31 @@ __global__ __launch_bounds__(K2_THREADS) void k2_contract(const K2Args p) {
     if (kt + C::STAGES - 1 < nk) issue(kt + C::STAGES - 1);
 
     const uint8_t* st = smem + (kt % C::STAGES) * C::STAGE_BYTES;
+    // fragments of sub-step s + 1 are read while the MFMAs of s run
+    bf16x8 af[2][C::MI], bfr[2][C::NJ];
+#pragma unroll
+    for (int mi = 0; mi < C::MI; ++mi) af[0][mi] = ld_frag(st + offA[mi][0]);
+#pragma unroll
+    for (int nj = 0; nj < C::NJ; ++nj) bfr[0][nj] = ld_frag(st + offB[nj][0]);
 #pragma unroll
     for (int s = 0; s < SUB; ++s) {
-      bf16x8 af[C::MI], bfr[C::NJ];
+      const int cur = s & 1;
+      if (s + 1 < SUB) {
 #pragma unroll
-      for (int mi = 0; mi < C::MI; ++mi) af[mi] = ld_frag(st + offA[mi][s]);
+        for (int mi = 0; mi < C::MI; ++mi) af[cur ^ 1][mi] = ld_frag(st + offA[mi][s + 1]);
 #pragma unroll
-      for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = ld_frag(st + offB[nj][s]);
+        for (int nj = 0; nj < C::NJ; ++nj) bfr[cur ^ 1][nj] = ld_frag(st + offB[nj][s + 1]);
+      }
       // D[j][i]: rows from plane b, columns from plane a, so each lane ends
       // with 4 consecutive j of one i (8 contiguous bytes of a y row)
 #pragma unroll
       for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-        for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = mfma32x32x16(bfr[nj], af[mi], acc[mi][nj]);
+        for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = mfma32x32x16(bfr[cur][nj], af[cur][mi], acc[mi][nj]);
+      // the reads first, then the MFMAs
+      if (s + 1 < SUB) __builtin_amdgcn_sched_group_barrier(0x100, C::MI + C::NJ, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, C::MI * C::NJ, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   lds_barrier();   // the ring is reused as the epilogue staging area
@@ -271,8 +280,7 @@ __global__ __launch_bounds__(K2_THREADS) void k2_contract_p(const K2Args p) {
   const uint32_t plane_bytes = uint32_t(p.c) * uint32_t(p.B) * uint32_t(N) * uint32_t(ld) * 2u;
   const auto rsrc_y = __builtin_amdgcn_make_buffer_rsrc(p.plane_y, 0, plane_bytes, 0x00020000);
 
-  const uint16_t* srcA[C::IA];
-  const uint16_t* srcB[C::IB];
+  uint32_t srcA[C::IA], srcB[C::IB];                    // byte offsets into the planes
   int i0 = 0, j0 = 0;
   uint32_t ybase = 0;                                   // element offset of the tile's matrix
   auto setup = [&](int logical) {
@@ -284,30 +292,28 @@ __global__ __launch_bounds__(K2_THREADS) void k2_contract_p(const K2Args p) {
     j0 = tn * C::BN;
     const size_t base = size_t(mat) * N * ld;
     ybase = uint32_t(base);
-    const uint16_t* Ag = p.plane_a + base;
-    const uint16_t* Bg = p.plane_b + base;
+    // (every plane is below 2^31 bytes; rows past N clamp to N - 1)
 #pragma unroll
     for (int t = 0; t < C::IA; ++t) {
       int r, c;
       C::src((wave * C::IA + t) * 64 + lane, r, c);
-      srcA[t] = Ag + size_t(min(i0 + r, N - 1)) * ld + 8 * c;   // rows past N clamp to N - 1
+      srcA[t] = uint32_t((base + size_t(min(i0 + r, N - 1)) * ld + 8 * c) * 2);
     }
 #pragma unroll
     for (int t = 0; t < C::IB; ++t) {
       int r, c;
       C::src((wave * C::IB + t) * 64 + lane, r, c);
-      srcB[t] = Bg + size_t(min(j0 + r, N - 1)) * ld + 8 * c;
+      srcB[t] = uint32_t((base + size_t(min(j0 + r, N - 1)) * ld + 8 * c) * 2);
     }
   };
   auto issue = [&](int kstep) {
     uint8_t* st = smem + (kstep % C::STAGES) * C::STAGE_BYTES;
-    const int k0 = kstep * C::BK;
+    const uint16_t* ga = p.plane_a + kstep * C::BK;
+    const uint16_t* gb = p.plane_b + kstep * C::BK;
 #pragma unroll
-    for (int t = 0; t < C::IA; ++t)
-      load_lds16(srcA[t] + k0, st + (wave * C::IA + t) * 1024);
+    for (int t = 0; t < C::IA; ++t) load_lds16_asm(ga, srcA[t], st + (wave * C::IA + t) * 1024);
 #pragma unroll
-    for (int t = 0; t < C::IB; ++t)
-      load_lds16(srcB[t] + k0, st + C::A_BYTES + (wave * C::IB + t) * 1024);
+    for (int t = 0; t < C::IB; ++t) load_lds16_asm(gb, srcB[t], st + C::A_BYTES + (wave * C::IB + t) * 1024);
   };
 
   constexpr int SUB = C::BK / 16;
@@ -346,18 +352,30 @@ __global__ __launch_bounds__(K2_THREADS) void k2_contract_p(const K2Args p) {
       // sub-step of MFMAs, instead of stalling behind waves 0-3's loads with
       // their matrix cores idle.
       const int fill_at = wave >= 4 ? 1 : 0;
+      // fragments of sub-step s + 1 are read while the MFMAs of s run
+      bf16x8 af[2][C::MI], bfr[2][C::NJ];
+#pragma unroll
+      for (int mi = 0; mi < C::MI; ++mi) af[0][mi] = ld_frag(st + offA[mi][0]);
+#pragma unroll
+      for (int nj = 0; nj < C::NJ; ++nj) bfr[0][nj] = ld_frag(st + offB[nj][0]);
 #pragma unroll
       for (int s = 0; s < SUB; ++s) {
         if (s == fill_at && kt + 1 < nk) issue(kt + 1);
-        bf16x8 af[C::MI], bfr[C::NJ];
+        const int cur = s & 1;
+        if (s + 1 < SUB) {
 #pragma unroll
-        for (int mi = 0; mi < C::MI; ++mi) af[mi] = ld_frag(st + offA[mi][s]);
+          for (int mi = 0; mi < C::MI; ++mi) af[cur ^ 1][mi] = ld_frag(st + offA[mi][s + 1]);
 #pragma unroll
-        for (int nj = 0; nj < C::NJ; ++nj) bfr[nj] = ld_frag(st + offB[nj][s]);
+          for (int nj = 0; nj < C::NJ; ++nj) bfr[cur ^ 1][nj] = ld_frag(st + offB[nj][s + 1]);
+        }
 #pragma unroll
         for (int mi = 0; mi < C::MI; ++mi)
 #pragma unroll
-          for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = mfma32x32x16(bfr[nj], af[mi], acc[mi][nj]);
+          for (int nj = 0; nj < C::NJ; ++nj) acc[mi][nj] = mfma32x32x16(bfr[cur][nj], af[cur][mi], acc[mi][nj]);
+        // the reads first, then the MFMAs
+        if (s + 1 < SUB) __builtin_amdgcn_sched_group_barrier(0x100, C::MI + C::NJ, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, C::MI * C::NJ, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     lds_barrier();   // every wave is done with the ring

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   auto load_y = [&](int row, int j0) {
     const char* base = reinterpret_cast<const char*>(p.plane_y + size_t(row) * p.n_pad + j0);
 #pragma unroll
-    for (int q = 0; q < NLD; ++q) load_lds16(base + yoff[q], sm.ys + (wave * NLD + q) * 1024);
+    for (int q = 0; q < NLD; ++q) load_lds16_asm(base, yoff[q], sm.ys + (wave * NLD + q) * 1024);
   };
   // x of a tile -> the z tile, 512 bytes per pair row, 16-byte chunk c of pair
   // lp at position c ^ (8 (lp & 1)) (conflict-free for the LayerNorm lane
@@ -157,7 +157,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
       const int pr = s >> 5, pos = s & 31;
       const int c = pos ^ ((pr & 1) << 3);
       const uint32_t off = (uint32_t(min(pr, last)) * CZ + 8u * uint32_t(c)) * 2u;
-      load_lds16(base + off, sm.z + (wave * NLD + q) * 1024);
+      load_lds16_asm(base, off, sm.z + (wave * NLD + q) * 1024);
     }
   };
 
