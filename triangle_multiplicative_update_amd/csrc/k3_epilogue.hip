@@ -132,18 +132,18 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   // y of a tile -> channel-major staging, 128 bytes (64 pairs) per row. Row r
   // holds channel r ^ ((r >> 1) & 1), so that the even (and the odd) channels
   // one 16-lane cycle of the transpose reads fall in both halves of the banks.
-  uint32_t yoff[NLD];                       // per-lane byte offsets from the tile's first y element
-#pragma unroll
-  for (int q = 0; q < NLD; ++q) {
-    const int s = (wave * NLD + q) * 64 + lane;          // 16-byte slot
-    const int r = s >> 3, jc = s & 7;
-    const int ch = r ^ ((r >> 1) & 1);
-    yoff[q] = (uint32_t(ch) * uint32_t(ch_stride) + 8u * uint32_t(jc)) * 2u;
-  }
+  // Load q of wave w fills slots s = (w NLD + q) 64 + lane: row r = s / 8,
+  // 8 pairs jc = s % 8. Rows 8 (w NLD + q) .. + 7 differ between loads only in
+  // that multiple of 8, which the channel flip leaves alone, so one lane offset
+  // plus a uniform 8 channels per load serves all NLD loads.
+  const int yr = lane >> 3;
+  const uint32_t yoff = (uint32_t(8 * wave * NLD + (yr ^ ((yr >> 1) & 1))) * uint32_t(ch_stride) +
+                         8u * uint32_t(lane & 7)) * 2u;
+  const uint32_t ystep = 8u * uint32_t(ch_stride) * 2u;
   auto load_y = [&](int row, int j0) {
     const char* base = reinterpret_cast<const char*>(p.plane_y + size_t(row) * p.n_pad + j0);
 #pragma unroll
-    for (int q = 0; q < NLD; ++q) load_lds16_asm(base, yoff[q], sm.ys + (wave * NLD + q) * 1024);
+    for (int q = 0; q < NLD; ++q) load_lds16_asm(base + q * ystep, yoff, sm.ys + (wave * NLD + q) * 1024);
   };
   // x of a tile -> the z tile, 512 bytes per pair row, 16-byte chunk c of pair
   // lp at position c ^ (8 (lp & 1)) (conflict-free for the LayerNorm lane
@@ -171,9 +171,10 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
     int row, j0, rown, j0n;
     tile_at(k, row, j0);
     tile_at(k + 1 < nk ? k + 1 : k, rown, j0n);      // the last tile loads itself again
-    // y and x of this tile have landed; the previous tile's stores may not have
-    if (k == 0) wait_vm<0>();
-    else wait_vm<NST>();
+    // y of this tile has landed: issued since, this tile's x loads (the
+    // previous tile's, after its MFMAs) and the previous tile's stores
+    if (k == 0) wait_vm<NLD>();
+    else wait_vm<NLD + NST>();
     lds_barrier();
 
     // ---- y staging -> pair-major rows (two channels per dword) ----
@@ -195,17 +196,6 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
         *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0 + 1, cp >> 2) + 4 * (cp & 3)) = odd;
       }
     }
-    // ---- LayerNorm_in in place: x rows of the z tile -> z_in ----
-    // (the 8 lanes of pair lp are in one wave and read the whole row before
-    // any of them writes it)
-    {
-      u32x4 xr[NV], z[NV];
-#pragma unroll
-      for (int v = 0; v < NV; ++v) xr[v] = ld16(sm.z + lp * (C * 2) + (((sub + 8 * v) ^ ((lp & 1) << 3)) << 4));
-      layer_norm_row_lds<NV>(xr, sm.inw, sm.inb, sub, p.eps, z);
-#pragma unroll
-      for (int v = 0; v < NV; ++v) st16(sm.z + soff<C>(lp, sub + 8 * v), z[v]);
-    }
     lds_barrier();
     load_y(rown, j0n);
 
@@ -217,6 +207,24 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
       layer_norm_row_lds<NV>(yr, sm.outw, sm.outb, sub, p.eps, u);
 #pragma unroll
       for (int v = 0; v < NV; ++v) st16(sm.y + soff<C>(lp, sub + 8 * v), u[v]);
+    }
+
+    // ---- LayerNorm_in in place: x rows of the z tile -> z_in ----
+    // x of this tile has landed: issued since, the previous tile's stores
+    // and the next tile's y loads. A wave's LayerNorm lanes read only the
+    // pair rows that wave loaded (rows 8w .. 8w + 7), so no barrier is needed
+    // between the wait and the reads; the 8 lanes of pair lp are in one wave
+    // and read the whole row before any of them writes it.
+    __builtin_amdgcn_sched_barrier(0);
+    if (k == 0) wait_vm<NLD>();
+    else wait_vm<NST + NLD>();
+    {
+      u32x4 xr[NV], z[NV];
+#pragma unroll
+      for (int v = 0; v < NV; ++v) xr[v] = ld16(sm.z + lp * (C * 2) + (((sub + 8 * v) ^ ((lp & 1) << 3)) << 4));
+      layer_norm_row_lds<NV>(xr, sm.inw, sm.inb, sub, p.eps, z);
+#pragma unroll
+      for (int v = 0; v < NV; ++v) st16(sm.z + soff<C>(lp, sub + 8 * v), z[v]);
     }
     lds_barrier();
 
