@@ -243,20 +243,29 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
           acc_g[4 * q + e] = bg4[e];
         }
       }
-      int prow = 32 * mb + l32;           // pair this lane feeds as the B operand
-      // an opaque copy per tile, so the fragment addresses derived from it are
-      // not hoisted out of the tile loop (they would hold 64 registers for the
-      // whole kernel)
-      asm volatile("" : "+v"(prow));
+      const int prow = 32 * mb + l32;     // pair this lane feeds as the B operand
+      // soff(prow, 2 ks + lhi) = fbase + 256 (ks >> 3) + 32 ((ks & 7) ^ ft):
+      // two opaque per-tile values instead of one address register per k-step
+      const int fs = lds_swz(prow);
+      int fbase = prow * (C * 2) + ((lhi ^ (fs & 1)) << 4);
+      int ft = fs >> 1;
+      asm volatile("" : "+v"(fbase), "+v"(ft));
+      auto faddr = [&](int ks) { return fbase + 256 * (ks >> 3) + ((((ks & 7) ^ ft)) << 5); };
+      // the u and z fragments of k-step ks + 1 are read before the MFMAs of ks
+      bf16x8 uf[2], zf[2];
+      uf[0] = ld_frag(sm.y + faddr(0));
+      zf[0] = ld_frag(sm.z + faddr(0));
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        // keep the compiler from loading every k-step's fragments ahead (128
-        // more registers); four k-steps in flight are enough
-        if (ks % 4 == 0 && ks > 0) asm volatile("" ::: "memory");
-        const bf16x8 u = ld_frag(sm.y + soff<C>(prow, 2 * ks + lhi));
-        const bf16x8 z = ld_frag(sm.z + soff<C>(prow, 2 * ks + lhi));
-        acc_p = mfma32x32x16(wp[ks], u, acc_p);
-        acc_g = mfma32x32x16(wg[ks], z, acc_g);
+        const int cur = ks & 1;
+        if (ks + 1 < KS) {
+          const int a = faddr(ks + 1);
+          uf[cur ^ 1] = ld_frag(sm.y + a);
+          zf[cur ^ 1] = ld_frag(sm.z + a);
+        }
+        acc_p = mfma32x32x16(wp[ks], uf[cur], acc_p);
+        acc_g = mfma32x32x16(wg[ks], zf[cur], acc_g);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // lane holds pair 32*mb + l32 and 4 consecutive channels per register group
 #pragma unroll
