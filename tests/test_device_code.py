@@ -49,3 +49,25 @@ def test_wide_buffer_stores_take_no_scalar_offset_register(name, tmp_path):
         assert not (dst and lo <= int(dst.group(1)) <= hi), f"{name}: {line.strip()} then {nxt}"
     if name != "k2_contract.hip":
         assert wide > 0, f"{name}: expected buffer stores"
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="hipcc not installed")
+@pytest.mark.parametrize("name", KERNELS)
+def test_m0_is_only_the_direct_loads_lds_address(name, tmp_path):
+    """The direct loads are inline assembly that sets M0 (the LDS address of
+    the copy) itself, which is only sound if no compiler-generated code keeps
+    a value in M0: every M0 reference must be that assembly's `s_mov_b32 m0`
+    with its direct load right behind it."""
+    lines = [l.strip() for l in _asm(os.path.join(tb.CSRC, name), tmp_path)]
+    code = [l for l in lines if l and not l.startswith((";", ".", "_"))]
+    loads = 0
+    for i, line in enumerate(code):
+        if "global_load_lds" in line:
+            loads += 1
+        if not re.search(r"\bm0\b", line):
+            continue
+        assert re.fullmatch(r"s_mov_b32 m0, s\d+", line), f"{name}: {line}"
+        follow = code[i + 1:i + 3]
+        assert follow[0] == "s_nop 0" and follow[1].startswith("global_load_lds_dwordx4"), f"{name}: {line} then {follow}"
+    assert loads > 0
