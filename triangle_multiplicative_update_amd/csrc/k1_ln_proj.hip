@@ -16,16 +16,17 @@
 // channels' value and gate weight rows (2 x 32 x c_z bf16) in registers for
 // the whole kernel, so the weights are read once per block, not per tile.
 //
-// Software pipeline. Each wave splits its multiply into two halves of 32
-// pairs and overlaps the matrix cores with the VALU across tile boundaries:
-// while the MFMAs of half 1 of tile t run, the wave applies sigmoid * value *
-// mask to half 0 of tile t; while the MFMAs of half 0 of tile t+1 run, it
-// finishes half 1 of tile t. Between the two, LayerNorm of tile t+1 goes into
-// the other z buffer and the x loads of tile t+2 are issued; after the one
-// barrier per tile, the block stores tile t-1's staged channel-major outputs
-// with 16-byte coalesced writes. z and the mask are double-buffered in LDS,
-// the output staging triple-buffered (double for c_z = 256, with a second
-// barrier), so no buffer is overwritten while another wave still reads it.
+// Software pipeline (c_z = 128, k1_ln_proj). Each wave splits its multiply
+// into two halves of 32 pairs and overlaps the matrix cores with the VALU
+// across tile boundaries: while the MFMAs of half 1 of tile t run, the wave
+// applies sigmoid * value * mask to half 0 of tile t; while the MFMAs of half
+// 0 of tile t+1 run, it finishes half 1 of tile t. Between the two, LayerNorm
+// of tile t+1 goes into the other z buffer and the x loads of tile t+2 are
+// issued; after the one barrier per tile, the block stores tile t-1's staged
+// channel-major outputs with 16-byte coalesced writes. z and the mask are
+// double-buffered in LDS, the output staging triple-buffered, so no buffer is
+// overwritten while another wave still reads it. The c_z = 256 form
+// (k1_ln_proj_wide, below) has its own pipeline.
 
 #include <type_traits>
 

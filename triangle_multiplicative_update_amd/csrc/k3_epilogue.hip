@@ -63,17 +63,20 @@ __device__ __forceinline__ int ooff(int r, int unit) {
 // loads while this tile is processed, y into a channel-major staging tile
 // (issued once this tile's y has been transposed out of it), x into the z
 // tile (issued once this tile's MFMAs have read z). Per tile:
-//   wait for y(t), x(t); barrier
-//   y staging -> pair-major y rows (two channels per dword); LayerNorm_in
-//   in place on the x rows of the z tile (stage-1 lane mapping); barrier
-//   issue y(t+1); LayerNorm_out in place on the y rows; barrier
+//   wait for y(t); barrier
+//   y staging -> pair-major y rows (two channels per dword); barrier
+//   issue y(t+1); LayerNorm_out in place on the y rows; wait for this
+//   wave's rows of x(t); LayerNorm_in in place on them (stage-1 lane
+//   mapping); barrier
 //   two (32-channel block, pair half) jobs per wave of the output projection
 //   and gate into the out staging; barrier
 //   issue x(t+1); pair-major stores of tile t
-// Every store is issued (a pair past N at an offset past the end of out,
-// dropped by the hardware), so the wait at the top of a tile is exact: only
-// the previous tile's stores may still be in flight. The LayerNorm affines
-// and output biases live in LDS as fp32.
+// x(t) is waited for after LayerNorm_out, so its loads (issued late in the
+// previous tile, the z tile being their only home) have the transpose and
+// LayerNorm_out to land behind. Every store is issued (a pair past N at an
+// offset past the end of out, dropped by the hardware), so both waits count
+// exactly: the previous tile's stores and the loads issued after the one
+// waited for. The LayerNorm affines and output biases live in LDS as fp32.
 template <int C>
 __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   static_assert(C == 256, "the c = 128 form is k3_epilogue_ws");
