@@ -54,6 +54,12 @@ CASES = [
     (2, 136, 256, "bernoulli", True),
     (1, 45, 256, "padded", False),
     (2, 100, 256, "bernoulli", True),    # 128 x 128 contraction tiles, 512 matrices
+    # c_z = 256 stage 1 at one tile per block and at one or two (192 tiles over
+    # 128 blocks), an exact 64-pair row, a single pair
+    (1, 96, 256, "padded", True),
+    (1, 64, 256, "bernoulli", False),
+    (2, 8, 256, "none", True),
+    (1, 1, 256, "ones", True),
     (3, 24, 128, "none", True),
     # several stage-2 tiles per persistent block, the last one ragged
     (1, 300, 128, "padded", True),
