@@ -82,7 +82,7 @@ def soff(r, slot, C=128):
     return r * (C * 2) + ((slot ^ lds_swz(r)) << 4)
 
 
-@pytest.mark.parametrize("C", [128, 256])
+@pytest.mark.parametrize("C", [128])
 def test_stage3_tiles_are_conflict_free(C):
     NV, KS = C // 64, C // 16
     # LayerNorm rows: pair tid >> 3 of the wave's 8, slot sub + 8 v
@@ -109,43 +109,91 @@ def test_stage3_tiles_are_conflict_free(C):
                     assert extra_cycles(addr, 4) == 0
 
 
-# ---- stage 3 at c = 256: the direct-load staging of the next tile ----
-def ys_row(ch):
-    """staging row of channel ch (row r holds channel r ^ ((r >> 1) & 1), an involution)"""
-    return ch ^ ((ch >> 1) & 1)
+# ---- stage 3 at c = 256 (k3_epilogue_h256): 32-pair half tiles of 512-byte rows ----
+def swz32(r):
+    return (1 if r & 1 else 0) ^ (8 if r & 2 else 0) ^ (4 if r & 8 else 0) ^ (10 if r & 16 else 0)
 
 
-def test_stage3_wide_staging_is_conflict_free_and_complete():
-    # the direct loads: slot s = 64 * (4 * wave + q) + lane of the y staging holds
-    # channel ys_row(s >> 3), pair chunk s & 7 -- every (channel, chunk) exactly once
-    seen = set()
-    for s in range(256 * 8):
-        r, jc = s >> 3, s & 7
-        seen.add((ys_row(r), jc))
-        assert ys_row(ys_row(r)) == r
+def soff32(r, slot):
+    return r * 512 + ((slot ^ swz32(r)) << 4)
+
+
+def test_stage3_half_tile_rows_are_conflict_free():
+    # LayerNorm rows (waves 0-3 on u, waves 4-7 on z): pair 8 w + l / 8, slot sub + 8 v
+    for w in range(4):
+        for v in range(4):
+            addr = [soff32(8 * w + (l >> 3), (l & 7) + 8 * v) for l in range(64)]
+            assert extra_cycles(addr, 16) == 0
+    # MFMA fragment reads: row l32, slot 2 ks + lhi
+    for ks in range(16):
+        addr = [soff32(l & 31, 2 * ks + (l >> 5)) for l in range(64)]
+        assert extra_cycles(addr, 16) == 0
+    # the same reads with stage 1's lds_swz would conflict on the transpose writes below
+    assert any(extra_cycles([soff(8 * (l & 3) + t, (32 * w + (l >> 2)) >> 2, 256) +
+                             4 * ((32 * w + (l >> 2)) & 3) for l in range(64)], 4)
+               for w in range(4) for t in range(8))
+
+
+def ys_addr(ch, c):
+    """k3_epilogue_h256's ys staging: LDS row r (128 bytes) holds channel r ^ ((r >> 1) & 1),
+    its 16-byte chunk c (8 pairs) at position c ^ (4 ((r >> 2) & 1))"""
+    r = ch ^ ((ch >> 1) & 1)
+    return r * 128 + ((c ^ (4 * ((r >> 2) & 1))) << 4)
+
+
+def test_stage3_half_tile_staging_is_conflict_free_and_complete():
+    # the direct y loads: load q of wave w, lane l fills bytes 8 KB w + 1 KB q + 16 l
+    # with channel 64 w + 8 q + ych(l) at chunk yc(l) -- every (channel, chunk) once
+    seen = {}
+    for w in range(4):
+        for q in range(8):
+            for l in range(64):
+                yr = l >> 3
+                ych = yr ^ ((yr >> 1) & 1)
+                yc = (l & 7) ^ (4 * ((yr >> 2) & 1))
+                ch = 64 * w + ych + 8 * q
+                assert ys_addr(ch, yc) == 8192 * w + 1024 * q + 16 * l
+                seen[(ch, yc)] = True
     assert len(seen) == 256 * 8
-    # the transpose reads (16 bytes): item id = it * 512 + t, channel pair cp = id >> 3,
-    # chunk jc = id & 7, channels 2 cp and 2 cp + 1 from their staging rows
-    for it in range(2):
-        for w0 in range(0, 512, 64):
-            for odd in (0, 1):
-                addr = []
-                for l in range(64):
-                    i = it * 512 + w0 + l
-                    addr.append(ys_row(2 * (i >> 3) + odd) * 128 + (i & 7) * 16)
-                assert extra_cycles(addr, 16) == 0
-    # x in the z tile: chunk c of pair lp at position c ^ 8 (lp & 1); LayerNorm_in
-    # lane (lp = t >> 3, sub = t & 7) reads chunks sub + 8 v
-    for w0 in range(0, 512, 64):
+    # the transpose: item it of lane l is channel pair cp = 32 w + 16 it + l / 4 at chunk
+    # 4 half + l % 4; reads from yrd[e] ^ 64 half, + 4 KB for item 1; writes of pair
+    # 8 jc + 2 q + e to u row bytes (uwr ^ 64 it ^ 16 e ^ 128 (q % 2)) + 512 (2 q + e)
+    for w in range(4):
+        for half in range(2):
+            for it in range(2):
+                for e in range(2):
+                    addr = []
+                    for l in range(64):
+                        jc, cpl = l & 3, l >> 2
+                        ch = 2 * (32 * w + cpl) + e
+                        r = ch ^ ((ch >> 1) & 1)
+                        yrd = r * 128 + jc * 16 + 64 * ((r >> 2) & 1)
+                        a = (yrd ^ (64 * half)) + 4096 * it
+                        assert a == ys_addr(2 * (32 * w + 16 * it + cpl) + e, 4 * half + jc)
+                        addr.append(a)
+                    assert extra_cycles(addr, 16) == 0
+                for q in range(4):
+                    for e in range(2):
+                        addr = []
+                        for l in range(64):
+                            jc, cpl = l & 3, l >> 2
+                            uwr = jc * 4096 + (((8 * w + (cpl >> 2)) ^ swz32(8 * jc)) << 4) + 4 * (cpl & 3)
+                            a = (uwr ^ (64 * it) ^ (16 * e) ^ (128 * (q & 1))) + 512 * (2 * q + e)
+                            cp = 32 * w + 16 * it + cpl
+                            assert a == soff32(8 * jc + 2 * q + e, cp >> 2) + 4 * (cp & 3)
+                            addr.append(a)
+                        assert extra_cycles(addr, 4) == 0
+    # x in xs: chunk c of pair lp at position c ^ 8 (lp & 1); LayerNorm_in lane
+    # (lp = 8 lw + l / 8, sub = l % 8) of waves 4-7 reads chunks sub + 8 v
+    for lw in range(4):
         for v in range(4):
             addr = []
             for l in range(64):
-                t = w0 + l
-                lp, sub = t >> 3, t & 7
+                lp, sub = 8 * lw + (l >> 3), l & 7
                 addr.append(lp * 512 + (((sub + 8 * v) ^ ((lp & 1) << 3)) << 4))
             assert extra_cycles(addr, 16) == 0
-    # the same reads without the permutations would conflict
-    plain = [((2 * (l >> 3)) * 128 + (l & 7) * 16) for l in range(64)]
+    # the y staging read in pair order without the permutations would conflict
+    plain = [(2 * (l >> 2)) * 128 + (l & 3) * 16 for l in range(64)]
     assert extra_cycles(plain, 16) > 0
 
 
@@ -154,17 +202,17 @@ def ooff(r, unit, C=128):
     return r * (C * 2) + ((unit ^ (r & 31)) << 3)
 
 
-@pytest.mark.parametrize("C", [128, 256])
-def test_stage3_out_staging_is_conflict_free(C):
+@pytest.mark.parametrize("C,rows", [(128, 64), (256, 32)])
+def test_stage3_out_staging_is_conflict_free(C, rows):
     # gate writes (8 bytes): pair row 32 mb + l32, unit 2 (4 nb + rg) + lhi
     for nb in range(C // 32):
-        for mb in range(2):
+        for mb in range(rows // 32):
             for rg in range(4):
                 addr = [ooff(32 * mb + (l & 31), 2 * (4 * nb + rg) + (l >> 5), C) for l in range(64)]
                 assert extra_cycles(addr, 8) == 0
     # store reads (16 bytes): chunk id = it * 256 + t, pair pr = id / (C / 8), chunk
     # cc = id % (C / 8), read from chunk cc ^ ((pr % 32) >> 1) of row pr
-    for it in range(64 * C // 8 // 256):
+    for it in range(rows * C // 8 // 256):
         for w0 in range(0, 256, 64):
             addr = []
             for l in range(64):

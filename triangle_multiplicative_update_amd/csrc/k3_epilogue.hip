@@ -10,16 +10,20 @@
 //
 // Work decomposition. A tile is 64 pairs (b, i, j0..j0+63): one 128-byte row
 // of each y plane and 64 contiguous pair rows of x and out; blocks of 8 waves
-// are persistent. Two forms: at c = 128 the waves specialise (k3_epilogue_ws:
-// four matrix waves, four LayerNorm waves, one of each per SIMD); at c = 256
-// every wave runs every phase (k3_epilogue<256>). Both transpose y to
-// pair-major LDS rows two channels per dword, run LayerNorm_in with the
-// stage-1 lane mapping (so z_in is bit-identical) and LayerNorm_out, compute
-// the value and gate with MFMA 32x32x16 as D[out channel][pair] (weights as
-// the A operand, held in registers), and stage sigmoid * value as bf16 in LDS
-// [pair][channel] for 16-byte coalesced stores. The y/u and z tiles use the
-// 256-byte-row slot swizzle (lds_swz); the out staging tile has its own
-// 8-byte-unit swizzle (ooff), both conflict-free for their accesses under
+// are persistent. Two forms: at c = 128 the waves specialise
+// (k3_epilogue_ws: four matrix waves, four LayerNorm waves, one of each per
+// SIMD); at c = 256, where every wave must hold 32 output channels' weights,
+// the waves specialise by phase instead (k3_epilogue_h256: each wave runs its
+// share of the MFMAs in one phase and LayerNorm work in the other, the two
+// waves of a SIMD in opposite phases, over half tiles of 32 pairs). Both
+// transpose y to pair-major LDS rows two channels per dword, run LayerNorm_in
+// with the stage-1 lane mapping (so z_in is bit-identical) and LayerNorm_out,
+// compute the value and gate with MFMA 32x32x16 as D[out channel][pair]
+// (weights as the A operand, held in registers), and stage sigmoid * value
+// as bf16 in LDS [pair][channel] for 16-byte coalesced stores. The pair-major
+// tiles use XOR slot swizzles (lds_swz for 256-byte rows, swz32 for the
+// 512-byte rows of a half tile); the out staging tile has its own
+// 8-byte-unit swizzle (ooff); all conflict-free for their accesses under
 // gfx950's LDS bank model.
 
 #include "trimul_device.hpp"
@@ -31,16 +35,6 @@ namespace {
 
 constexpr int K3_THREADS = 512;
 constexpr int K3_TP = 64;
-
-template <int C>
-struct K3Smem {
-  static constexpr int RB = C * 2;         // row bytes (pair-major, no padding)
-  uint8_t y[K3_TP * RB];                   // y, then u
-  uint8_t z[K3_TP * RB];                   // x of the tile (direct loads), then z_in in place
-  uint8_t o[K3_TP * RB];                   // out staging
-  uint8_t ys[C * K3_TP * 2];               // y of the next tile, channel-major (direct loads)
-  float inw[C], inb[C], outw[C], outb[C], bp[C], bg[C];   // LayerNorm affines, output biases
-};
 
 // byte offset of 16-byte slot `slot` of pair row `r` in a swizzled tile
 template <int C>
@@ -57,39 +51,69 @@ __device__ __forceinline__ int ooff(int r, int unit) {
   return r * (C * 2) + ((unit ^ (r & 31)) << 3);
 }
 
-// c = 256 form. Every wave runs every phase of a tile. The 32 output
-// channels' weights of a wave take 128 registers, so nothing is prefetched
-// into registers: the next tile's y and x travel by direct global -> LDS
-// loads while this tile is processed, y into a channel-major staging tile
-// (issued once this tile's y has been transposed out of it), x into the z
-// tile (issued once this tile's MFMAs have read z). Per tile:
-//   wait for y(t); barrier
-//   y staging -> pair-major y rows (two channels per dword); barrier
-//   issue y(t+1); LayerNorm_out in place on the y rows; wait for this
-//   wave's rows of x(t); LayerNorm_in in place on them (stage-1 lane
-//   mapping); barrier
-//   two (32-channel block, pair half) jobs per wave of the output projection
-//   and gate into the out staging; barrier
-//   issue x(t+1); pair-major stores of tile t
-// x(t) is waited for after LayerNorm_out, so its loads (issued late in the
-// previous tile, the z tile being their only home) have the transpose and
-// LayerNorm_out to land behind. Every store is issued (a pair past N at an
-// offset past the end of out, dropped by the hardware), so both waits count
-// exactly: the previous tile's stores and the loads issued after the one
-// waited for. The LayerNorm affines and output biases live in LDS as fp32.
-template <int C>
-__global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
-  static_assert(C == 256, "the c = 128 form is k3_epilogue_ws");
-  constexpr int CZ = C;                    // c_z == c
+// ---------------------------------------------------------------------------
+// c = 256, phase-specialised form. The unit of work is a half tile of 32
+// pairs (b, i, j0 .. j0 + 31), the two halves of each 64-pair tile one after
+// the other. Every wave holds the p_out and g_out rows of its 32 output
+// channels (128 registers) and runs its share of every half tile's MFMAs, but
+// the two waves of a SIMD do so in opposite phases, each running vector-ALU
+// work while the other's matrix cores run (MFMA and vector issue share a
+// SIMD, so the waves' instruction streams, not their phases, set the time).
+// Iteration h (half tile h's MFMAs, buffers b = h % 2):
+//   phase 1: waves 0-3 run their channel blocks of h (u[b], z[b] -> o[b]);
+//            between the MFMAs of the first k-steps they transpose their
+//            64-channel slices of the y of half tile h + 1 (ys -> u[b^1]),
+//            and after the second half of a tile, issue the next tile's y
+//            loads over the remaining k-steps, so that the issue waits
+//            overlap the MFMAs. Waves 4-7 run LayerNorm_in of h + 1 on their
+//            8 pairs (xs -> z[b^1], the stage-1 lane mapping), issuing the x
+//            loads of h + 2 into xs once the rows are in registers.
+//   phase 2: waves 4-7 run their channel blocks of h (-> o[b]); waves 0-3
+//            run LayerNorm_out of h + 1 in place on their 8 pairs of u[b^1]
+//            and store half tile h - 1 from o[b^1].
+// y is staged per 64-pair tile as full 128-byte lines (both halves at once;
+// loading each half's 64 bytes separately doubles the requests and stalls
+// the issue), x per half tile. Each kind of wave loads only the LDS bytes it
+// reads itself, so its loads need no barrier, only its own wait count: waves
+// 4-7 issue nothing but x loads (wait for all), waves 0-3 a tile's y loads
+// and then one iteration's stores (wait for all but those stores). Stores of
+// half tiles that do not exist go past the end of out, so every iteration
+// issues the same stores.
+constexpr int K3H_TP = 32;                 // pairs per half tile
+constexpr int K3H_PF = 2;                  // fragment ring depth (k-steps in flight + 1)
+
+// Pair rows of 512 bytes (256 bf16 channels) of a 32-row tile: 16-byte slot s
+// of row r at slot s ^ swz32(r), row bits XOR-ed in as bit 0 -> 1, bit 1 -> 8,
+// bit 3 -> 4, bit 4 -> 10 (bit 2 -> 0). Under the LDS bank model this keeps
+// the MFMA fragment reads (32 consecutive rows at one slot, the upper 32 lanes
+// at the next), the LayerNorm rows (8 lanes x 16 bytes per row, 8 rows) and
+// the transposing 4-byte writes (4 rows {8 j + e} x 16 consecutive dwords)
+// conflict-free.
+__device__ __forceinline__ int swz32(int r) {
+  return ((r & 1) ? 1 : 0) ^ ((r & 2) ? 8 : 0) ^ ((r & 8) ? 4 : 0) ^ ((r & 16) ? 10 : 0);
+}
+__device__ __forceinline__ int soff32(int r, int slot) { return r * 512 + ((slot ^ swz32(r)) << 4); }
+
+struct K3HSmem {
+  static constexpr int TB = K3H_TP * 512;  // one 32-pair tile of 512-byte rows
+  uint8_t u[2][TB];                        // transposed y rows, then u in place
+  uint8_t z[2][TB];                        // z_in
+  uint8_t o[2][TB];                        // out staging
+  uint8_t ys[2 * TB];                      // y of a whole 64-pair tile as loaded (see load_y)
+  uint8_t xs[TB];                          // x of a half tile as loaded
+  float inw[256], inb[256], outw[256], outb[256], bp[256], bg[256];
+};
+
+__global__ __launch_bounds__(K3_THREADS) void k3_epilogue_h256(const K3Args p) {
+  constexpr int C = 256, CZ = 256;
   constexpr int NV = C / 64;               // LayerNorm chunks per lane
   constexpr int KS = C / 16;               // MFMA k-steps
-  constexpr int NB = CZ / 32;              // 32-channel output blocks
-  constexpr int JOBS = 2 * NB / 8;         // (channel block, pair half) jobs per wave
-  constexpr int NY = (C / 2) * 8 / K3_THREADS;   // (channel pair, 8-pair chunk) items per thread
-  constexpr int NST = (K3_TP * CZ / 8) / K3_THREADS;   // 16-byte out chunks per thread per tile
-  constexpr int NLD = K3_TP * C * 2 / 1024 / 8;        // 1 KB direct loads per wave per tile and tensor
-  static_assert(NLD == 4 && NST == 4, "wait counts below assume 4 loads and 4 stores per wave");
-  using S = K3Smem<C>;
+  constexpr int NLD = 4;                   // 1 KB x loads per wave of waves 4-7 per half tile
+  constexpr int NLY = 8;                   // 1 KB y loads per wave of waves 0-3 per 64-pair tile
+  constexpr int NST = 4;                   // 16-byte out stores per lane of waves 4-7 per half tile
+  static_assert(NLD * 4 * 1024 == K3HSmem::TB && NST * 256 * 16 == K3HSmem::TB, "one tile per wave kind");
+  static_assert(NLY * 4 * 1024 == sizeof(K3HSmem::ys), "y of a 64-pair tile");
+  using S = K3HSmem;
   __shared__ __attribute__((aligned(16))) S sm;
 
   const int tid = threadIdx.x;
@@ -102,13 +126,14 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   const int G = gridDim.x;
   const int nk = int(blockIdx.x) < p.ntiles ? (p.ntiles - int(blockIdx.x) + G - 1) / G : 0;
   if (nk == 0) return;                      // the whole block: no barrier is left unmatched
-  auto tile_at = [&](int k, int& row, int& j0) {
-    const int t = int(blockIdx.x) + k * G;
+  const int nh = 2 * nk;                    // half tiles of this block
+  auto half_at = [&](int h, int& row, int& j0) {
+    const int t = int(blockIdx.x) + (h >> 1) * G;
     row = fast_div(t, p.div_nchunk);                     // b * N + i
-    j0 = (t - row * p.nchunk) * K3_TP;
+    j0 = (t - row * p.nchunk) * K3_TP + K3H_TP * (h & 1);
   };
 
-  // ---- wave jobs: output channel block nb, both pair halves ----
+  // ---- this wave's output channels 32 nb .. 32 nb + 31 ----
   const int nb = wave;
   const int nrow = 32 * nb + l32;          // weight row (output channel) this lane feeds
   bf16x8 wp[KS], wg[KS];
@@ -117,10 +142,6 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
     wp[ks] = ld_frag(p.p_out + size_t(nrow) * C + 16 * ks + 8 * lhi);
     wg[ks] = ld_frag(p.g_out + size_t(nrow) * CZ + 16 * ks + 8 * lhi);
   }
-
-  // ---- LayerNorm lane mapping (same as stage 1): pair lp, sub-lane sub ----
-  const int lp = tid >> 3;
-  const int sub = tid & 7;
   stage_f32(sm.inw, p.ln_in_w, CZ);
   stage_f32(sm.inb, p.ln_in_b, CZ);
   stage_f32(sm.outw, p.ln_out_w, C);
@@ -128,177 +149,261 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue(const K3Args p) {
   stage_f32(sm.bp, p.p_out_b, CZ);
   stage_f32(sm.bg, p.g_out_b, CZ);
 
-  const size_t ch_stride = size_t(p.B) * N * p.n_pad;
-  const uint32_t xo_bytes = uint32_t(p.B) * uint32_t(N) * uint32_t(N) * uint32_t(CZ) * 2u;
-  const auto rsrc_o = __builtin_amdgcn_make_buffer_rsrc(p.out, 0, xo_bytes, 0x00020000);
-
-  // y of a tile -> channel-major staging, 128 bytes (64 pairs) per row. Row r
-  // holds channel r ^ ((r >> 1) & 1), so that the even (and the odd) channels
-  // one 16-lane cycle of the transpose reads fall in both halves of the banks.
-  // Load q of wave w fills slots s = (w NLD + q) 64 + lane: row r = s / 8,
-  // 8 pairs jc = s % 8. Rows 8 (w NLD + q) .. + 7 differ between loads only in
-  // that multiple of 8, which the channel flip leaves alone, so one lane offset
-  // plus a uniform 8 channels per load serves all NLD loads.
-  const int yr = lane >> 3;
-  const uint32_t yoff = (uint32_t(8 * wave * NLD + (yr ^ ((yr >> 1) & 1))) * uint32_t(ch_stride) +
-                         8u * uint32_t(lane & 7)) * 2u;
-  const uint32_t ystep = 8u * uint32_t(ch_stride) * 2u;
-  auto load_y = [&](int row, int j0) {
-    const char* base = reinterpret_cast<const char*>(p.plane_y + size_t(row) * p.n_pad + j0);
+  // output projection and gate of half tile in buffers b for this wave's 32
+  // channels: D[out channel][pair], then sigmoid * value as bf16 into o[b]
+  auto mma_gate = [&](int b, auto&& at_kstep) {
+    f32x16 acc_p, acc_g;
 #pragma unroll
-    for (int q = 0; q < NLD; ++q) load_lds16_asm(base + q * ystep, yoff, sm.ys + (wave * NLD + q) * 1024);
-  };
-  // x of a tile -> the z tile, 512 bytes per pair row, 16-byte chunk c of pair
-  // lp at position c ^ (8 (lp & 1)) (conflict-free for the LayerNorm lane
-  // mapping); a pair past N reads pair N - 1 (its results are not stored)
-  auto load_x = [&](int row, int j0) {
-    const char* base = reinterpret_cast<const char*>(p.x + (size_t(row) * N + j0) * CZ);
-    const int last = N - 1 - j0;
+    for (int q = 0; q < 4; ++q) {   // 4 consecutive output channels per register group
+      const int n = 32 * nb + 8 * q + 4 * lhi;
+      const f32x4 bp4 = *reinterpret_cast<const f32x4*>(&sm.bp[n]);
+      const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&sm.bg[n]);
 #pragma unroll
-    for (int q = 0; q < NLD; ++q) {
-      const int s = (wave * NLD + q) * 64 + lane;
-      const int pr = s >> 5, pos = s & 31;
-      const int c = pos ^ ((pr & 1) << 3);
-      const uint32_t off = (uint32_t(min(pr, last)) * CZ + 8u * uint32_t(c)) * 2u;
-      load_lds16_asm(base, off, sm.z + (wave * NLD + q) * 1024);
+      for (int e = 0; e < 4; ++e) {
+        acc_p[4 * q + e] = bp4[e];
+        acc_g[4 * q + e] = bg4[e];
+      }
+    }
+    // soff32(l32, 2 ks + lhi) = fbase + 256 (ks >> 3) + 32 ((ks & 7) ^ ft)
+    const int fs = swz32(l32);
+    int fbase = l32 * 512 + ((lhi ^ (fs & 1)) << 4);
+    int ft = fs >> 1;
+    asm volatile("" : "+v"(fbase), "+v"(ft));
+    auto faddr = [&](int ks) { return fbase + 256 * (ks >> 3) + ((((ks & 7) ^ ft)) << 5); };
+    const uint8_t* ub = sm.u[b];
+    const uint8_t* zb = sm.z[b];
+    // the fragments of k-step ks + PF - 1 are read before the MFMAs of ks: the
+    // other wave of the SIMD runs vector work, not MFMAs, while this one waits
+    bf16x8 uf[K3H_PF], zf[K3H_PF];
+#pragma unroll
+    for (int i = 0; i < K3H_PF - 1; ++i) {
+      uf[i] = ld_frag(ub + faddr(i));
+      zf[i] = ld_frag(zb + faddr(i));
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks + K3H_PF - 1 < KS) {
+        const int a = faddr(ks + K3H_PF - 1);
+        uf[(ks + K3H_PF - 1) % K3H_PF] = ld_frag(ub + a);
+        zf[(ks + K3H_PF - 1) % K3H_PF] = ld_frag(zb + a);
+      }
+      acc_p = mfma32x32x16(wp[ks], uf[ks % K3H_PF], acc_p);
+      acc_g = mfma32x32x16(wg[ks], zf[ks % K3H_PF], acc_g);
+      at_kstep(ks);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int rg = 0; rg < 4; ++rg) {
+      float o[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = sigmoid_f(acc_g[4 * rg + q]) * acc_p[4 * rg + q];
+      const u32x2 packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      *reinterpret_cast<u32x2*>(sm.o[b] + ooff<C>(l32, 2 * (4 * nb + rg) + lhi)) = packed;
     }
   };
 
-  {
-    int row, j0;
-    tile_at(0, row, j0);
-    load_y(row, j0);
-    load_x(row, j0);
-  }
-  for (int k = 0; k < nk; ++k) {
-    int row, j0, rown, j0n;
-    tile_at(k, row, j0);
-    tile_at(k + 1 < nk ? k + 1 : k, rown, j0n);      // the last tile loads itself again
-    // y of this tile has landed: issued since, this tile's x loads (the
-    // previous tile's, after its MFMAs) and the previous tile's stores
-    if (k == 0) wait_vm<NLD>();
-    else wait_vm<NLD + NST>();
-    lds_barrier();
-
-    // ---- y staging -> pair-major rows (two channels per dword) ----
-    // item: channel pair cp = id / 8, pair chunk jc = id % 8
+  const int sub = lane & 7;                 // sub-lane of a LayerNorm pair (stage-1 mapping)
+  if (wave < 4) {
+    // ---- waves 0-3: y of channels 64 w .. 64 w + 63, LayerNorm_out of pairs 8 w .. 8 w + 7 ----
+    const int w = wave;
+    // y of a whole 64-pair tile goes to ys once, as full 128-byte lines of
+    // the y planes. LDS row R (128 bytes) holds channel R ^ ((R >> 1) & 1),
+    // its 16-byte chunk c (8 pairs) at position c ^ (4 ((R >> 2) & 1)), so
+    // that the transpose reads of either half tile are conflict-free. Load q
+    // of this wave fills rows 64 w + 8 q .. + 7 (channels of its own slice):
+    // lane l gets row 64 w + 8 q + l / 8 at position l % 8, one lane offset
+    // plus a uniform 8 channels per load.
+    const size_t ch_stride = size_t(p.B) * N * p.n_pad;
+    const int yr = lane >> 3;
+    const int ych = yr ^ ((yr >> 1) & 1);
+    const int yc = (lane & 7) ^ (4 * ((yr >> 2) & 1));
+    const uint32_t yoff = (uint32_t(64 * w + ych) * uint32_t(ch_stride) + 8u * uint32_t(yc)) * 2u;
+    const uint32_t cs2 = uint32_t(ch_stride) * 2u;
+    auto y_base = [&](int t) {               // the block's 64-pair tile t
+      int row, j0;
+      half_at(2 * t, row, j0);
+      return reinterpret_cast<const char*>(p.plane_y + size_t(row) * p.n_pad + j0);
+    };
+    auto load_y = [&](const char* base, int q) {
+      load_lds16_asm(base + 8u * uint32_t(q) * cs2, yoff, sm.ys + (NLY * w + q) * 1024);
+    };
+    // Transpose of half tile `half` of ys: item it of lane l is channel pair
+    // cp = 32 w + 16 it + l / 4 (channels 2 cp, 2 cp + 1) at pairs 8 jc ..
+    // 8 jc + 7 of the half, jc = l % 4. Both layouts are XOR swizzles, so
+    // every address is one of a few lane values XOR-ed with a constant plus a
+    // constant offset: the read of channel 2 cp + e is yrd[e] ^ 64 half, + 4 KB
+    // for item 1; pair 8 jc + 2 q + e of item it goes to u row bytes
+    // (uwr ^ 64 it ^ 16 e ^ 128 (q % 2)) + 512 (2 q + e).
+    const int jc = lane & 3, cpl = lane >> 2;
+    int yrd[2];
 #pragma unroll
-    for (int it = 0; it < NY; ++it) {
-      const int id = it * K3_THREADS + tid;
-      const int cp = id >> 3;
-      const int jc = id & 7;
-      const int flip = cp & 1;              // rows of channels 2 cp, 2 cp + 1 (see load_y)
-      const u32x4 ya = ld16(sm.ys + ((2 * cp) ^ flip) * 128 + 16 * jc);
-      const u32x4 yb = ld16(sm.ys + ((2 * cp + 1) ^ flip) * 128 + 16 * jc);
+    for (int e = 0; e < 2; ++e) {
+      const int ch = 2 * (32 * w + cpl) + e;
+      const int r = ch ^ ((ch >> 1) & 1);
+      yrd[e] = r * 128 + jc * 16 + 64 * ((r >> 2) & 1);
+    }
+    const int uwr = jc * 4096 + (((8 * w + (cpl >> 2)) ^ swz32(8 * jc)) << 4) + 4 * (cpl & 3);
+    u32x4 ya, yb;
+    auto tr_read = [&](int half, int it) {
+      ya = ld16(sm.ys + (yrd[0] ^ (64 * half)) + 4096 * it);
+      yb = ld16(sm.ys + (yrd[1] ^ (64 * half)) + 4096 * it);
+    };
+    // part j of 2 of item it: pairs 8 jc + 4 j .. + 3
+    auto tr_write = [&](int b, int it, int j) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
+      for (int qq = 0; qq < 2; ++qq) {
+        const int q = 2 * j + qq;
         const uint32_t even = __builtin_amdgcn_perm(yb[q], ya[q], 0x05040100u);   // pair 8jc + 2q
         const uint32_t odd = __builtin_amdgcn_perm(yb[q], ya[q], 0x07060302u);    // pair 8jc + 2q + 1
-        const int r0 = 8 * jc + 2 * q;
-        *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0, cp >> 2) + 4 * (cp & 3)) = even;
-        *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0 + 1, cp >> 2) + 4 * (cp & 3)) = odd;
+        const int a = uwr ^ (64 * it) ^ (128 * (q & 1));
+        *reinterpret_cast<uint32_t*>(sm.u[b] + a + 512 * (2 * q)) = even;
+        *reinterpret_cast<uint32_t*>(sm.u[b] + (a ^ 16) + 512 * (2 * q + 1)) = odd;
       }
-    }
-    lds_barrier();
-    load_y(rown, j0n);
-
-    // ---- LayerNorm_out in place on the pair rows of y ----
-    {
+    };
+    auto transpose = [&](int b, int half) {
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        tr_read(half, it);
+        tr_write(b, it, 0);
+        tr_write(b, it, 1);
+      }
+    };
+    // the transpose spread over the first k-steps of the MFMAs
+    auto tr_at = [&](int ks, int b, int half) {
+      if (ks == 0) tr_read(half, 0);
+      if (ks == 2) tr_write(b, 0, 0);
+      if (ks == 3) tr_write(b, 0, 1);
+      if (ks == 3) tr_read(half, 1);
+      if (ks == 5) tr_write(b, 1, 0);
+      if (ks == 6) tr_write(b, 1, 1);
+    };
+    const uint32_t xo_bytes = uint32_t(p.B) * uint32_t(N) * uint32_t(N) * uint32_t(CZ) * 2u;
+    const auto rsrc_o = __builtin_amdgcn_make_buffer_rsrc(p.out, 0, xo_bytes, 0x00020000);
+    // pair-major stores of half tile h from o[h % 2]; a pair past N, or a
+    // half tile outside the block's, goes past the end of out (0x80000000
+    // plus a tile base below 2^31 stays below 2^32) and is dropped
+    auto store = [&](int h) {
+      const bool valid = h >= 0 && h < nh;
+      int row, j0;
+      half_at(valid ? h : 0, row, j0);
+      const int so = __builtin_amdgcn_readfirstlane((row * N + j0) * CZ * 2);
+      const uint8_t* ob = sm.o[h & 1];
+#pragma unroll
+      for (int it = 0; it < NST; ++it) {
+        const int id = it * 256 + tid;
+        const int pr = id / (CZ / 8);
+        const int cc = id - pr * (CZ / 8);
+        u32x4 v = ld16(ob + pr * 512 + ((cc ^ ((pr & 31) >> 1)) << 4));
+        if (pr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
+        const uint32_t off = (valid && j0 + pr < N) ? uint32_t(id) * 16u : 0x80000000u;
+        buffer_store16(rsrc_o, v, off + uint32_t(so));
+      }
+    };
+    const int lp = 8 * w + (lane >> 3);
+    auto ln_out = [&](int b) {
       u32x4 yr[NV], u[NV];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) yr[v] = ld16(sm.y + soff<C>(lp, sub + 8 * v));
+      for (int v = 0; v < NV; ++v) yr[v] = ld16(sm.u[b] + soff32(lp, sub + 8 * v));
       layer_norm_row_lds<NV>(yr, sm.outw, sm.outb, sub, p.eps, u);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) st16(sm.y + soff<C>(lp, sub + 8 * v), u[v]);
-    }
+      for (int v = 0; v < NV; ++v) st16(sm.u[b] + soff32(lp, sub + 8 * v), u[v]);
+    };
 
-    // ---- LayerNorm_in in place: x rows of the z tile -> z_in ----
-    // x of this tile has landed: issued since, the previous tile's stores
-    // and the next tile's y loads. A wave's LayerNorm lanes read only the
-    // pair rows that wave loaded (rows 8w .. 8w + 7), so no barrier is needed
-    // between the wait and the reads; the 8 lanes of pair lp are in one wave
-    // and read the whole row before any of them writes it.
-    __builtin_amdgcn_sched_barrier(0);
-    if (k == 0) wait_vm<NLD>();
-    else wait_vm<NST + NLD>();
     {
+      const char* base = y_base(0);
+#pragma unroll
+      for (int q = 0; q < NLY; ++q) load_y(base, q);
+    }
+    lds_barrier();                           // the staged affines
+    wait_vm<0>();
+    transpose(0, 0);
+    lds_barrier();                           // y rows of half tile 0 (z of half tile 0)
+    ln_out(0);
+    lds_barrier();                           // u of half tile 0
+    for (int h = 0; h < nh; ++h) {
+      const int b = h & 1;
+      // half tile h + 1: the second half of the tile in ys, or the first
+      // half of the next tile, whose loads went out one iteration ago
+      // (followed by that iteration's stores)
+      // The transpose runs between the MFMAs of the first k-steps; once it
+      // has read both halves of tile h / 2 out of ys, the next tile's y goes
+      // in, one load per k-step, so that the issue waits overlap the MFMAs.
+      if (h + 1 < nh) {
+        if ((h & 1) == 1) wait_vm<NST>();
+        const int bn = b ^ 1, half = (h + 1) & 1;
+        if ((h & 1) == 0 && (h >> 1) + 1 < nk) {
+          const char* base = y_base((h >> 1) + 1);
+          mma_gate(b, [&](int ks) {
+            tr_at(ks, bn, half);
+            if (ks == 7) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (ks >= 8) load_y(base, ks - 8);
+          });
+        } else {
+          mma_gate(b, [&](int ks) { tr_at(ks, bn, half); });
+        }
+      } else {
+        mma_gate(b, [](int) {});
+      }
+      lds_barrier();
+      if (h + 1 < nh) ln_out(b ^ 1);
+      store(h - 1);
+      lds_barrier();
+    }
+    store(nh - 1);
+  } else {
+    // ---- waves 4-7: x and LayerNorm_in of pairs 8 lw .. 8 lw + 7, the stores ----
+    const int lw = wave - 4;
+    // x of a half tile -> xs, 512 bytes per pair row, 16-byte chunk c of pair
+    // lp at position c ^ (8 (lp & 1)); a pair past N reads pair N - 1 (its
+    // results are not stored). Load q of this wave fills rows 8 lw + 2 q,
+    // 8 lw + 2 q + 1: the rows its LayerNorm lanes read.
+    auto load_x = [&](int h) {
+      int row, j0;
+      half_at(min(h, nh - 1), row, j0);
+      const char* base = reinterpret_cast<const char*>(p.x + size_t(row) * N * CZ);
+#pragma unroll
+      for (int q = 0; q < NLD; ++q) {
+        const int s = (NLD * lw + q) * 64 + lane;
+        const int pr = s >> 5, pos = s & 31;
+        const int c = pos ^ ((pr & 1) << 3);
+        const uint32_t off = (uint32_t(min(j0 + pr, N - 1)) * CZ + 8u * uint32_t(c)) * 2u;
+        load_lds16_asm(base, off, sm.xs + (NLD * lw + q) * 1024);
+      }
+    };
+    const int lp = 8 * lw + (lane >> 3);
+    // LayerNorm_in of the x in xs into z[b]; once the row is in registers,
+    // xs takes the next loads (`then`)
+    auto ln_in = [&](int b, auto&& then) {
       u32x4 xr[NV], z[NV];
 #pragma unroll
-      for (int v = 0; v < NV; ++v) xr[v] = ld16(sm.z + lp * (C * 2) + (((sub + 8 * v) ^ ((lp & 1) << 3)) << 4));
+      for (int v = 0; v < NV; ++v) xr[v] = ld16(sm.xs + lp * 512 + (((sub + 8 * v) ^ ((lp & 1) << 3)) << 4));
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      then();
       layer_norm_row_lds<NV>(xr, sm.inw, sm.inb, sub, p.eps, z);
 #pragma unroll
-      for (int v = 0; v < NV; ++v) st16(sm.z + soff<C>(lp, sub + 8 * v), z[v]);
-    }
-    lds_barrier();
-
-    // ---- output projection and gate: D[out channel][pair] ----
-#pragma unroll
-    for (int mb = 0; mb < JOBS; ++mb) {
-      f32x16 acc_p, acc_g;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {   // 4 consecutive output channels per register group
-        const int n = 32 * nb + 8 * q + 4 * lhi;
-        const f32x4 bp4 = *reinterpret_cast<const f32x4*>(&sm.bp[n]);
-        const f32x4 bg4 = *reinterpret_cast<const f32x4*>(&sm.bg[n]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          acc_p[4 * q + e] = bp4[e];
-          acc_g[4 * q + e] = bg4[e];
-        }
+      for (int v = 0; v < NV; ++v) st16(sm.z[b] + soff32(lp, sub + 8 * v), z[v]);
+    };
+    load_x(0);
+    lds_barrier();                           // the staged affines
+    wait_vm<0>();
+    ln_in(0, [&] { load_x(1); });
+    lds_barrier();                           // z of half tile 0 (y rows of half tile 0)
+    lds_barrier();                           // u of half tile 0
+    for (int h = 0; h < nh; ++h) {
+      const int b = h & 1;
+      if (h + 1 < nh) {
+        wait_vm<0>();                        // x of half tile h + 1 (all this wave has in flight)
+        ln_in(b ^ 1, [&] {
+          if (h + 2 < nh) load_x(h + 2);
+        });
       }
-      const int prow = 32 * mb + l32;     // pair this lane feeds as the B operand
-      // soff(prow, 2 ks + lhi) = fbase + 256 (ks >> 3) + 32 ((ks & 7) ^ ft):
-      // two opaque per-tile values instead of one address register per k-step
-      const int fs = lds_swz(prow);
-      int fbase = prow * (C * 2) + ((lhi ^ (fs & 1)) << 4);
-      int ft = fs >> 1;
-      asm volatile("" : "+v"(fbase), "+v"(ft));
-      auto faddr = [&](int ks) { return fbase + 256 * (ks >> 3) + ((((ks & 7) ^ ft)) << 5); };
-      // the u and z fragments of k-step ks + 1 are read before the MFMAs of ks
-      bf16x8 uf[2], zf[2];
-      uf[0] = ld_frag(sm.y + faddr(0));
-      zf[0] = ld_frag(sm.z + faddr(0));
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const int cur = ks & 1;
-        if (ks + 1 < KS) {
-          const int a = faddr(ks + 1);
-          uf[cur ^ 1] = ld_frag(sm.y + a);
-          zf[cur ^ 1] = ld_frag(sm.z + a);
-        }
-        acc_p = mfma32x32x16(wp[ks], uf[cur], acc_p);
-        acc_g = mfma32x32x16(wg[ks], zf[cur], acc_g);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // lane holds pair 32*mb + l32 and 4 consecutive channels per register group
-#pragma unroll
-      for (int rg = 0; rg < 4; ++rg) {
-        float o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) o[q] = sigmoid_f(acc_g[4 * rg + q]) * acc_p[4 * rg + q];
-        const u32x2 packed = {pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-        *reinterpret_cast<u32x2*>(sm.o + ooff<C>(prow, 2 * (4 * nb + rg) + lhi)) = packed;
-      }
-    }
-    lds_barrier();
-    load_x(rown, j0n);
-
-    // ---- pair-major stores of out (a pair past N goes past the end of out:
-    // 0x80000000 plus a tile base below 2^31 stays below 2^32, and is dropped) ----
-    const int so = __builtin_amdgcn_readfirstlane((row * N + j0) * CZ * 2);
-#pragma unroll
-    for (int it = 0; it < NST; ++it) {
-      const int id = it * K3_THREADS + tid;
-      const int pr = id / (CZ / 8);
-      const int cc = id - pr * (CZ / 8);
-      u32x4 v = ld16(sm.o + pr * (C * 2) + ((cc ^ ((pr & 31) >> 1)) << 4));
-      if (pr & 1) v = u32x4{v[2], v[3], v[0], v[1]};
-      const uint32_t off = j0 + pr < N ? uint32_t(id) * 16u : 0x80000000u;
-      buffer_store16(rsrc_o, v, off + uint32_t(so));
+      lds_barrier();
+      mma_gate(b, [](int) {});
+      lds_barrier();
     }
   }
-  // the last tile's loads of itself: nothing may still be writing the LDS
-  // when the block ends
+  // the last loads (of the block's last half tile again): nothing may still
+  // be writing the LDS when the block ends
   wait_vm<0>();
 }
 
@@ -609,7 +714,7 @@ hipError_t launch_k3(const K3Args& a, int grid_x, hipStream_t stream) {
   if (a.c == 128) {
     hipLaunchKernelGGL(k3_epilogue_ws, dim3(grid_x), dim3(K3_THREADS), 0, stream, a);
   } else if (a.c == 256) {
-    hipLaunchKernelGGL(k3_epilogue<256>, dim3(grid_x), dim3(K3_THREADS), 0, stream, a);
+    hipLaunchKernelGGL(k3_epilogue_h256, dim3(grid_x), dim3(K3_THREADS), 0, stream, a);
   } else {
     return hipErrorInvalidValue;
   }

@@ -58,7 +58,7 @@ def stage_of(kernel_name: str):
     ``trimul::k2_contract_p(trimul::K2Args)`` or
     ``trimul::(anonymous namespace)::k3_epilogue_ws(trimul::K3Args)``."""
     for s, n in KERNEL_NAMES.items():
-        if re.search(r"\b" + n + r"(_ws|_p|_wide)?(<|\()", kernel_name):
+        if re.search(r"\b" + n + r"(_ws|_p|_wide|_h256)?(<|\()", kernel_name):
             return s
     return None
 
