@@ -260,13 +260,14 @@ __device__ __forceinline__ void ln_apply(const u32x4 (&x)[NV], float mean, float
   }
 }
 
-// The row unpacked once and kept as 8 * NV floats across both reductions
-// (any NV; layer_norm_row_wb takes this form for NV <= 2).
 template <int NV, class WB>
-__device__ __forceinline__ void layer_norm_row_kept_wb(const u32x4 (&xin)[NV], WB&& affine, float eps,
-                                                       u32x4 (&zout)[NV]) {
+__device__ __forceinline__ void layer_norm_row_wb(const u32x4 (&xin)[NV], WB&& affine, float eps,
+                                                  u32x4 (&zout)[NV]) {
 #pragma clang fp contract(off)
-  {
+  if constexpr (NV > 2) {
+    const float mean = ln_mean<NV>(xin);
+    ln_apply<NV>(xin, mean, ln_rstd<NV>(xin, mean, eps), affine, zout);
+  } else {
     constexpr float inv_n = 1.0f / float(64 * NV);
     float v[NV][8];
 #pragma unroll
@@ -308,18 +309,6 @@ __device__ __forceinline__ void layer_norm_row_kept_wb(const u32x4 (&xin)[NV], W
       zout[c] = u32x4{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
                       pack_bf16x2(o[6], o[7])};
     }
-  }
-}
-
-template <int NV, class WB>
-__device__ __forceinline__ void layer_norm_row_wb(const u32x4 (&xin)[NV], WB&& affine, float eps,
-                                                  u32x4 (&zout)[NV]) {
-#pragma clang fp contract(off)
-  if constexpr (NV > 2) {
-    const float mean = ln_mean<NV>(xin);
-    ln_apply<NV>(xin, mean, ln_rstd<NV>(xin, mean, eps), affine, zout);
-  } else {
-    layer_norm_row_kept_wb<NV>(xin, affine, eps, zout);
   }
 }
 
@@ -460,13 +449,6 @@ __device__ __forceinline__ void layer_norm_row_lds(const u32x4 (&xin)[NV], const
                                                    int sub, float eps, u32x4 (&zout)[NV]) {
   layer_norm_row_wb<NV>(xin, [&](int c, float (&wv)[8], float (&bv)[8]) { lds_affine8(w, b, sub, c, wv, bv); },
                         eps, zout);
-}
-// the same with the row kept unpacked (the same bits; 8 * NV more live floats)
-template <int NV>
-__device__ __forceinline__ void layer_norm_row_lds_kept(const u32x4 (&xin)[NV], const float* w, const float* b,
-                                                        int sub, float eps, u32x4 (&zout)[NV]) {
-  layer_norm_row_kept_wb<NV>(xin, [&](int c, float (&wv)[8], float (&bv)[8]) { lds_affine8(w, b, sub, c, wv, bv); },
-                             eps, zout);
 }
 
 // Widen a bf16 vector of length n into an fp32 LDS array (block-cooperative;
