@@ -110,7 +110,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_h256(const K3Args p) {
   constexpr int KS = C / 16;               // MFMA k-steps
   constexpr int NLD = 4;                   // 1 KB x loads per wave of waves 4-7 per half tile
   constexpr int NLY = 8;                   // 1 KB y loads per wave of waves 0-3 per 64-pair tile
-  constexpr int NST = 4;                   // 16-byte out stores per lane of waves 4-7 per half tile
+  constexpr int NST = 4;                   // 16-byte out stores per lane of waves 0-3 per half tile
   static_assert(NLD * 4 * 1024 == K3HSmem::TB && NST * 256 * 16 == K3HSmem::TB, "one tile per wave kind");
   static_assert(NLY * 4 * 1024 == sizeof(K3HSmem::ys), "y of a 64-pair tile");
   using S = K3HSmem;
@@ -214,9 +214,9 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_h256(const K3Args p) {
     // lane l gets row 64 w + 8 q + l / 8 at position l % 8, one lane offset
     // plus a uniform 8 channels per load.
     const size_t ch_stride = size_t(p.B) * N * p.n_pad;
-    const int yr = lane >> 3;
-    const int ych = yr ^ ((yr >> 1) & 1);
-    const int yc = (lane & 7) ^ (4 * ((yr >> 2) & 1));
+    const int yrow = lane >> 3;
+    const int ych = yrow ^ ((yrow >> 1) & 1);
+    const int yc = (lane & 7) ^ (4 * ((yrow >> 2) & 1));
     const uint32_t yoff = (uint32_t(64 * w + ych) * uint32_t(ch_stride) + 8u * uint32_t(yc)) * 2u;
     const uint32_t cs2 = uint32_t(ch_stride) * 2u;
     auto y_base = [&](int t) {               // the block's 64-pair tile t
@@ -322,12 +322,12 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_h256(const K3Args p) {
     lds_barrier();                           // u of half tile 0
     for (int h = 0; h < nh; ++h) {
       const int b = h & 1;
-      // half tile h + 1: the second half of the tile in ys, or the first
+      // Half tile h + 1 is the second half of the tile in ys, or the first
       // half of the next tile, whose loads went out one iteration ago
-      // (followed by that iteration's stores)
-      // The transpose runs between the MFMAs of the first k-steps; once it
-      // has read both halves of tile h / 2 out of ys, the next tile's y goes
-      // in, one load per k-step, so that the issue waits overlap the MFMAs.
+      // (followed by that iteration's stores). Its transpose runs between
+      // the MFMAs of the first k-steps; once both halves of tile h / 2 have
+      // been read out of ys, the next tile's y goes in, one load per k-step,
+      // so that the issue waits overlap the MFMAs.
       if (h + 1 < nh) {
         if ((h & 1) == 1) wait_vm<NST>();
         const int bn = b ^ 1, half = (h + 1) & 1;
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_h256(const K3Args p) {
     }
     store(nh - 1);
   } else {
-    // ---- waves 4-7: x and LayerNorm_in of pairs 8 lw .. 8 lw + 7, the stores ----
+    // ---- waves 4-7: x and LayerNorm_in of pairs 8 lw .. 8 lw + 7 ----
     const int lw = wave - 4;
     // x of a half tile -> xs, 512 bytes per pair row, 16-byte chunk c of pair
     // lp at position c ^ (8 (lp & 1)); a pair past N reads pair N - 1 (its
@@ -402,8 +402,8 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_h256(const K3Args p) {
       lds_barrier();
     }
   }
-  // the last loads (of the block's last half tile again): nothing may still
-  // be writing the LDS when the block ends
+  // every direct load has been waited for above; nothing may still be
+  // writing the LDS when the block ends
   wait_vm<0>();
 }
 
