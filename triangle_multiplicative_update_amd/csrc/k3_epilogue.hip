@@ -417,15 +417,18 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_h256(const K3Args p) {
 // wave, writing z and u for the matrix waves. Each SIMD holds one wave of each
 // kind, so the matrix cores of one overlap the vector ALU work of the other.
 // Iteration k has two barriers:
-//   phase 1: matrix waves run tile k's MFMAs (u/z buffer k % 2), then
-//            transpose the y of tile k+1 (in registers) into the shared y
-//            rows; LayerNorm waves write z of tile k+1
-//   phase 2: matrix waves run both pair halves' gates, store tile k-1 and load
-//            y of tile k+3; LayerNorm waves write u of tile k+1.
-// The LayerNorm waves load x of tile k+3 in phase 1, right after their
-// LayerNorm_in has read the register set the loads go to (two register sets:
-// x has 2 iterations to land, y 1.5); phase 2 then holds the matrix waves'
-// y loads and stores alone.
+//   phase 1: matrix waves run tile k's MFMAs (u/z buffer k % 2); LayerNorm
+//            waves write z of tile k+1
+//   phase 2: matrix waves run both pair halves' gates, transpose the y of
+//            tile k+2 (in registers) into y rows k % 2, store tile k-1 and
+//            load y of tile k+4; LayerNorm waves write u of tile k+1 from y
+//            rows (k+1) % 2.
+// With two sets of y rows the transpose runs a tile ahead, in the phase the
+// LayerNorm waves' LayerNorm_out makes the longer one. The LayerNorm waves
+// load x of tile k+3 in phase 1, right after their LayerNorm_in has read the
+// register set the loads go to (two register sets each: x and y have 2
+// iterations to land); phase 2 then holds the matrix waves' y loads and
+// stores alone.
 // Loads are issued in every iteration (clamped to the block's last tile) and
 // the stores too (past the end of out where there is nothing to store):
 // vector-memory operations retire in issue order and the compiler counts the
@@ -438,7 +441,7 @@ struct K3WsSmem {
   uint8_t u[2][K3_TP * RB];                // LayerNorm_out rows
   uint8_t z[2][K3_TP * RB];                // LayerNorm_in rows
   uint8_t o[2][K3_TP * RB];                // out staging
-  uint8_t y[K3_TP * RB];                   // transposed y rows of the next tile
+  uint8_t y[2][K3_TP * RB];                // transposed y rows of the next two tiles
   float bp[128], bg[128];                  // output biases, fp32 (the accumulators' initial values)
 };
 
@@ -585,46 +588,45 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
           const int r0 = 8 * jc + 2 * q;
           const uint32_t even = __builtin_amdgcn_perm(yb[it][q], ya[it][q], 0x05040100u);   // pair r0
           const uint32_t odd = __builtin_amdgcn_perm(yb[it][q], ya[it][q], 0x07060302u);    // pair r0 + 1
-          *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0, cp >> 2) + 4 * (cp & 3)) = even;
-          *reinterpret_cast<uint32_t*>(sm.y + soff<C>(r0 + 1, cp >> 2) + 4 * (cp & 3)) = odd;
+          *reinterpret_cast<uint32_t*>(sm.y[e] + soff<C>(r0, cp >> 2) + 4 * (cp & 3)) = even;
+          *reinterpret_cast<uint32_t*>(sm.y[e] + soff<C>(r0 + 1, cp >> 2) + 4 * (cp & 3)) = odd;
         }
       }
     };
-    // prologue: the y rows of tile 0, with y of tiles 1 and 2 in flight in
-    // the order the loop issues them: a tile's y, one iteration's stores
-    // (past the end of out here), the next tile's y (into the set tile 0's
-    // transpose has just read)
+    // prologue: the y rows of tiles 0 and 1, with y of tiles 2 and 3 in
+    // flight, each into the register set its tile's transpose has just read
+    // (the stores of a first iteration go past the end of out)
     prefetch_y(0, I0{});
     prefetch_y(1, I1{});
     store(-2);
     transpose(I0{});
     prefetch_y(2, I0{});
-    lds_barrier();                           // y rows of tile 0 (the LayerNorm waves: z of tile 0)
+    transpose(I1{});
+    prefetch_y(3, I1{});
+    lds_barrier();                           // y rows of tiles 0, 1 (the LayerNorm waves: z of tile 0)
     lds_barrier();                           // u of tile 0
-    // iteration k: tile k's matrix work; the y of tile k + 1 (set (k + 1) % 2)
-    // transposed, then refilled with tile k + 3
+    // iteration k: tile k's matrix work; the y of tile k + 2 (set k % 2)
+    // transposed, then refilled with tile k + 4
     auto iteration = [&](int k, auto set) {
       const int b = k & 1;
       f32x16 p0, g0, p1, g1;
       if (k < nk) {
-        // both gates wait for phase 2: phase 1, with the transpose, is the
-        // matrix waves' longer phase
         mma(b, 0, p0, g0);
         mma(b, 1, p1, g1);
       }
-      if (k + 1 < nk) transpose(set);
       lds_barrier();
       if (k < nk) {
         gate(b, 0, p0, g0);
         gate(b, 1, p1, g1);
       }
+      if (k + 2 < nk) transpose(set);
       store(k - 1);
-      prefetch_y(k + 3, set);
+      prefetch_y(k + 4, set);
       lds_barrier();
     };
     for (int k = 0; k < nit; k += 2) {
-      iteration(k, I1{});
-      iteration(k + 1, I0{});
+      iteration(k, I0{});
+      iteration(k + 1, I1{});
     }
   } else {
     // ---- LayerNorm wave lw: normalises pairs 16 lw .. 16 lw + 15 ----
@@ -672,8 +674,8 @@ __global__ __launch_bounds__(K3_THREADS) void k3_epilogue_ws(const K3Args p) {
       u32x4 y0[NV], y1[NV], u0[NV], u1[NV];
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
-        y0[v] = ld16(sm.y + soff<C>(P0, sub + 8 * v));
-        y1[v] = ld16(sm.y + soff<C>(P1, sub + 8 * v));
+        y0[v] = ld16(sm.y[b] + soff<C>(P0, sub + 8 * v));
+        y1[v] = ld16(sm.y[b] + soff<C>(P1, sub + 8 * v));
       }
       layer_norm_rows2<NV>(y0, y1, outw, outb, p.eps, u0, u1);
 #pragma unroll
