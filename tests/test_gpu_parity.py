@@ -104,7 +104,7 @@ def test_fractional_mask(gpu, direction):
 # drawn once from a fixed generator (N from 1 to 320 across the 64-pair and
 # 128 / 256 contraction tile edges, B up to 3, both widths, every mask kind,
 # biases on or off, both directions).
-def _sweep_cases(n=16, seed=20261202):
+def _sweep_cases(n=24, seed=20261202):
     rng = np.random.default_rng(seed)
     cases = []
     for _ in range(n):
